@@ -1,0 +1,60 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins in test_oracle_pins.py catch every one of them.
+
+Each mutant is a textual edit of h3oracle.c (the pattern must occur exactly
+once), compiled with the same flags into a temporary library; the pin suite is
+then run against it in a subprocess and must fail.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "h3oracle.c")
+
+MUTANTS = {
+    "adaln_drop_one_plus_scale": ("xhat * (1.0 + sc) + sh", "xhat * sc + sh"),
+    "adaln_swap_shift_scale": ("xhat * (1.0 + sc) + sh", "xhat * (1.0 + sh) + sc"),
+    "adaln_unbiased_variance": ("const double var = ss / (double)D;",
+                                "const double var = ss / (double)(D - 1);"),
+    "adaln_eps_outside_sqrt": ("sqrt(var + eps)", "(sqrt(var) + eps)"),
+    "gated_transposed": ("xv + gv * hv", "gv * xv + hv"),
+    "swiglu_sign": ("a / (1.0 + exp(-a))", "a / (1.0 + exp(a))"),
+    "swiglu_wrong_half": ("const double a = ld(gate_up, dtype, r * 2 * inner + j);",
+                          "const double a = ld(gate_up, dtype, r * 2 * inner + inner + j);"),
+    "rms_drop_eps": ("sqrt(ss / (double)Dh + eps)", "sqrt(ss / (double)Dh)"),
+    "rms_wrong_weight": ("qk_head(k_out, k, k_weight,", "qk_head(k_out, k, q_weight,"),
+    "rope_clockwise": ("u[e1] = a * sn + b * cs;", "u[e1] = -a * sn + b * cs;"),
+    "rope_freq_exponent": ("pow(theta, -2.0 * (double)j / (double)dims[c])",
+                           "pow(theta, -1.0 * (double)j / (double)dims[c])"),
+    "rope_pairing": ("e0 = start + 2 * j;\n                e1 = start + 2 * j + 1;",
+                     "e0 = start + j;\n                e1 = start + j + dc / 2;"),
+    "rope_axis_order": ("const int32_t dims[3] = {d_t, d_h, d_w};\n    float inv_freq",
+                        "const int32_t dims[3] = {d_w, d_h, d_t};\n    float inv_freq"),
+    "positions_h_w_swapped": ("h = (int32_t)((p / W) % H);", "h = (int32_t)((p / H) % W);"),
+    "audio_position_axis": ("t = (int32_t)(p - n_video);\n            h = 0;",
+                            "t = 0;\n            h = (int32_t)(p - n_video);"),
+    "bf16_round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u + 0 * lsb;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation pattern for {name} must occur exactly once"
+    mutated = src.replace(old, new)
+    csrc = tmp_path / "h3oracle.c"
+    csrc.write_text(mutated)
+    hdr = os.path.join(ROOT, "oracle")
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    "-I", hdr, "-o", str(lib), str(csrc), "-lm"], check=True)
+    env = dict(os.environ, H3_ORACLE_LIB_OVERRIDE=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
