@@ -1,0 +1,215 @@
+/*
+ * h3fused.h -- C ABI of libh3fused: fused, memory-bound per-token operators of
+ * a single-stream audio+video diffusion transformer (MiniMax-H3 style DiT),
+ * implemented as hand-written HIP kernels for gfx950 (MI355X, CDNA4).
+ *
+ * Sources.  The operators are the ones the LMSYS performance report on
+ * MiniMax-H3 with SGLang Diffusion names as fused kernels (summary page on
+ * news.cocoloop.cn, "minimax-h3-sglang-h200", section "Só com três
+ * camadas…": AdaLN update, gated residual, SwiGLU, QK RMSNorm with 3D RoPE,
+ * fused to cut round trips through GPU memory without changing any result),
+ * also listed by the ceviu.com.br newsletter "SGLang acelera MiniMax-H3 em
+ * GPUs H200…".  The model facts (one dense single-stream transformer over a
+ * joint video+audio token sequence; a VisualVAE with 16x spatial / 4x temporal
+ * compression; an AdaLN branch whose outputs are token independent and can be
+ * precomputed) come from the studioglobal.ai explainer "MiniMax H3 mở trọng
+ * số…", section "Kiến trúc…", and the arex-research.com article on H3 and
+ * TPUs, section "H3 的开源底子".  The pages print no formula; each entry point
+ * states the standard definition it computes.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers (hipMalloc / torch CUDA tensors) unless a
+ *     parameter says otherwise.  The caller owns all memory; the library
+ *     keeps no pointer after a call returns and allocates nothing.
+ *   - Tensors are row-major with unit inner stride; every *_row_stride /
+ *     *_head_stride / *_group_stride is in ELEMENTS of that tensor's type.
+ *   - Vector width: 8 elements when any tensor of the call is bf16, else 4
+ *     elements (fp32 only).  hidden / inner / head_dim and every stride must
+ *     be multiples of it, and every pointer must be 16-byte aligned.
+ *   - Arithmetic is fp32 whatever the storage type; each output element is
+ *     rounded once (round to nearest even) to its storage type.
+ *   - Modulation vectors (shift, scale, gate) are [groups, hidden] rows: token
+ *     row r uses group g = r / rows_per_group (rows_per_group = rows gives one
+ *     vector for the whole call; 1 gives per-token modulation).
+ *   - rows == 0 is a no-op that returns H3F_OK before any other check.
+ *   - Validation is synchronous and happens before any launch; a bad argument
+ *     returns an error code and launches nothing.  No call aborts or throws.
+ *   - Aliasing: an output may be exactly the same tensor as an input (same
+ *     pointer, same strides, same type); any other overlap between an output
+ *     and another tensor of the call is H3F_ERR_ALIASING.  Tensors that are
+ *     interleaved with the same row stride (q, k, v of one packed qkv buffer)
+ *     do not overlap and are accepted.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream).  A fault inside a kernel surfaces at the caller's next
+ *     synchronisation.  Launch failures return H3F_ERR_LAUNCH.
+ *   - Every entry point is reentrant and keeps no state between calls.
+ */
+#ifndef H3FUSED_H
+#define H3FUSED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3F_ABI_VERSION 1
+
+typedef enum { H3F_F32 = 0, H3F_BF16 = 1 } h3f_dtype_t;
+
+typedef enum {
+    H3F_OK = 0,
+    H3F_ERR_NULL_POINTER = 1,
+    H3F_ERR_BAD_SHAPE = 2,
+    H3F_ERR_BAD_STRIDE = 3,
+    H3F_ERR_MISALIGNED = 4,
+    H3F_ERR_BAD_DTYPE = 5,
+    H3F_ERR_ALIASING = 6,
+    H3F_ERR_LAUNCH = 7,
+    H3F_ERR_UNSUPPORTED = 8
+} h3f_status_t;
+
+/* RoPE pair layouts inside one axis chunk of size d_c */
+typedef enum {
+    H3F_ROPE_INTERLEAVED = 0, /* pairs (2j, 2j+1)      (RoFormer, eq. 34)          */
+    H3F_ROPE_HALF_SPLIT = 1   /* pairs (j, j + d_c/2)  (rotate-half layout)        */
+} h3f_rope_pairing_t;
+
+/*
+ * Token grid and RoPE parameters of one joint video+audio sequence.
+ *   The sequence holds T*H*W video tokens in raster order (t slowest, w
+ *   fastest) followed by n_audio audio tokens; audio token k sits at
+ *   (t = k, h = 0, w = 0).  Row r of a call is global token
+ *   p = (token_offset + r) mod (T*H*W + n_audio), so a batch of B sequences
+ *   stacked along rows, or a shard of a sequence, is described by the same
+ *   struct.  (The pages fix the VAE factors that set T, H, W -- studioglobal.ai
+ *   explainer, section "Kiến trúc…" -- but neither the token order nor the
+ *   audio positions; these are readings.)
+ *   The head dimension is split into axis chunks [t | h | w] of sizes d_t, d_h,
+ *   d_w (d_t + d_h + d_w == head_dim, each a positive multiple of the vector
+ *   width, each a multiple of 16 for H3F_ROPE_HALF_SPLIT).  Pair j of chunk c
+ *   rotates by phi = fl32(fl32(pos_c) * fl32(theta^(-2j/d_c))).
+ *   positions: optional device int32 [rows, 3] array of (t, h, w) that, when
+ *   not NULL, replaces the grid derivation (T, H, W, n_audio, token_offset are
+ *   then ignored).
+ */
+typedef struct {
+    int32_t T, H, W, n_audio;
+    int32_t d_t, d_h, d_w;
+    int32_t pairing; /* h3f_rope_pairing_t */
+    double theta;    /* RoPE base, 10000 in RoFormer */
+    int64_t token_offset;
+    const int32_t* positions;
+} h3f_rope3d_t;
+
+/* Library ABI version (H3F_ABI_VERSION of the build). */
+int h3f_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* h3f_status_string(h3f_status_t status);
+
+/*
+ * Token positions: writes pos[r] = (t, h, w) of row r as described for
+ * h3f_rope3d_t (positions member ignored).  pos: device int32 [rows, 3],
+ * 4-byte aligned.  Integer work, bit-exact.
+ * Errors: NULL pos or grid; T, H, W < 1 or n_audio < 0 (BAD_SHAPE).
+ */
+h3f_status_t h3f_rope3d_positions(int32_t* pos, int64_t rows, const h3f_rope3d_t* grid,
+                                  void* stream);
+
+/*
+ * AdaLN modulate (fused LayerNorm + modulation; the report's "AdaLN update").
+ *   y[r,:] = (x[r,:] - mean_r) / sqrt(var_r + eps) * (1 + scale[g,:]) + shift[g,:]
+ * mean and (biased) var over the hidden dimension; LayerNorm has no affine of
+ * its own (DiT adaLN: Peebles & Xie 2023).
+ *   y: [rows, hidden] of y_dtype, row stride y_row_stride.
+ *   x: [rows, hidden] of x_dtype, row stride x_row_stride.
+ *   shift, scale: [groups, hidden] of x_dtype, group stride mod_group_stride.
+ * Supported (x, y) types: (f32, f32), (bf16, bf16), (f32, bf16).
+ * hidden <= 16384 (bf16 x) or 8192 (f32 x); else H3F_ERR_UNSUPPORTED.
+ * y may be x itself (same pointer, stride and type).
+ */
+h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t y_row_stride,
+                                const void* x, h3f_dtype_t x_dtype, int64_t x_row_stride,
+                                const void* shift, const void* scale, int64_t mod_group_stride,
+                                int64_t rows_per_group, int64_t rows, int64_t hidden, float eps,
+                                void* stream);
+
+/*
+ * Gated residual (the report's "residual com gate"), in place:
+ *   x[r,:] = x[r,:] + gate[g,:] * h[r,:]
+ *   x: [rows, hidden] of x_dtype (read and written); h: [rows, hidden] of
+ *   h_dtype; gate: [groups, hidden] of x_dtype.
+ * Supported (x, h) types: (f32, f32), (bf16, bf16), (f32, bf16).
+ * h must not overlap x.
+ */
+h3f_status_t h3f_gated_residual(void* x, h3f_dtype_t x_dtype, int64_t x_row_stride,
+                                const void* h, h3f_dtype_t h_dtype, int64_t h_row_stride,
+                                const void* gate, int64_t gate_group_stride,
+                                int64_t rows_per_group, int64_t rows, int64_t hidden,
+                                void* stream);
+
+/*
+ * SwiGLU (Shazeer 2020): out[r,j] = a[r,j] * sigmoid(a[r,j]) * b[r,j].
+ *   out, a, b: [rows, inner] of dtype, each with its own row stride.  For the
+ *   usual packed gate/up projection output gu [rows, 2*inner] pass
+ *   a = gu, b = gu + inner, a_row_stride = b_row_stride = 2*inner.
+ * out may be a or b itself (same pointer and stride).
+ */
+h3f_status_t h3f_swiglu(void* out, int64_t out_row_stride, const void* a, int64_t a_row_stride,
+                        const void* b, int64_t b_row_stride, h3f_dtype_t dtype, int64_t rows,
+                        int64_t inner, void* stream);
+
+/*
+ * Per-head QK RMSNorm + 3D RoPE (the report's "QK RMSNorm com 3D RoPE").
+ * For every row r, head i and tensor (q, k), with v the head's head_dim values:
+ *   u = v / sqrt(mean(v^2) + eps) * w        (RMSNorm, Zhang & Sennrich 2019;
+ *                                             w = q_weight or k_weight [head_dim])
+ *   each rotation pair (u0, u1) of axis chunk c at position pos_c(r):
+ *   (u0, u1) <- (u0 cos phi - u1 sin phi, u0 sin phi + u1 cos phi)
+ * Element (r, i, d) of q is at q + r*q_row_stride + i*q_head_stride + d, and
+ * likewise for k, q_out, k_out (a packed qkv [rows, 3, heads, head_dim]
+ * buffer gives q_row_stride = 3*heads*head_dim, k = q + heads*head_dim).
+ * q_out / k_out may be q / k themselves (same pointer and strides).
+ * head_dim / vector width must be a power of two <= 64 (head_dim <= 512 for
+ * bf16, <= 256 for f32); head strides >= head_dim.
+ */
+h3f_status_t h3f_qk_rmsnorm_rope3d(void* q_out, int64_t q_out_row_stride,
+                                   int64_t q_out_head_stride, void* k_out,
+                                   int64_t k_out_row_stride, int64_t k_out_head_stride,
+                                   const void* q, int64_t q_row_stride, int64_t q_head_stride,
+                                   const void* k, int64_t k_row_stride, int64_t k_head_stride,
+                                   const void* q_weight, const void* k_weight,
+                                   h3f_dtype_t dtype, int64_t rows, int32_t heads,
+                                   int32_t head_dim, float eps, const h3f_rope3d_t* rope,
+                                   void* stream);
+
+/*
+ * Gated residual followed by AdaLN modulate on the updated stream, in one
+ * pass over x (the two operators the report lists together, composed in the
+ * order a DiT block runs them):
+ *   x[r,:] = x[r,:] + gate[g,:] * h[r,:]            (stored rounded to x_dtype)
+ *   y[r,:] = AdaLN(x[r,:]; shift[g,:], scale[g,:])  (computed from the stored x)
+ * Same types, limits and rules as h3f_gated_residual and h3f_adaln_modulate;
+ * gate, shift and scale share mod_group_stride; y must not overlap x or h.
+ */
+h3f_status_t h3f_gated_residual_adaln(void* x, h3f_dtype_t x_dtype, int64_t x_row_stride,
+                                      const void* h, h3f_dtype_t h_dtype, int64_t h_row_stride,
+                                      const void* gate, const void* shift, const void* scale,
+                                      int64_t mod_group_stride, int64_t rows_per_group,
+                                      void* y, h3f_dtype_t y_dtype, int64_t y_row_stride,
+                                      int64_t rows, int64_t hidden, float eps, void* stream);
+
+/*
+ * Streaming copy (measurement helper, not an operator): dst[0:bytes) =
+ * src[0:bytes) with 16-byte vector loads and stores.  Used to measure the
+ * achievable HBM bandwidth and to calibrate hardware byte counters.  bytes
+ * must be a multiple of 16; dst and src must not overlap.
+ */
+h3f_status_t h3f_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* H3FUSED_H */

@@ -1,0 +1,229 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+symbol include/h3fused.h declares, and rejects invalid arguments with the
+documented status codes before any launch (no compute call is made here:
+every call below fails validation, which is pure host logic)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import video_diffusion_transformer_h3f_amd as h3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3fused.h")
+
+OK, NULLP, SHAPE, STRIDE, MISAL, DTYPE, ALIAS, LAUNCH, UNSUP = range(9)
+F32, BF16 = 0, 1
+
+
+def declared():
+    src = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:h3f_status_t|int|const char\s*\*)\s*(h3f_\w+)\s*\(", src,
+                          re.M))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared() == set(h3.EXPORTS)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = h3.lib()
+    for name in declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", h3.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (h3f_\w+)", out))
+    assert declared() <= exported
+    assert h3.abi_version() == 1
+
+
+def test_status_strings():
+    L = h3.lib()
+    for s in range(9):
+        assert L.h3f_status_string(s)
+    assert L.h3f_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+
+
+def A(n):
+    """A fake, never dereferenced device address, 16-byte aligned, far apart per n."""
+    return P(0x10000000 * (n + 1))
+
+
+L = None
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _lib():
+    global L
+    L = h3.lib()
+
+
+# --- gated residual -------------------------------------------------------------------
+
+def gated(x=A(0), xd=BF16, xs=256, h=A(1), hd=BF16, hs=256, gate=A(2), gs=0, rpg=10, rows=10,
+          hidden=256):
+    return L.h3f_gated_residual(x, xd, xs, h, hd, hs, gate, gs, rpg, rows, hidden, None)
+
+
+def test_gated_validation():
+    assert gated(x=None, rows=0) == OK  # rows == 0 is a no-op before any check
+    assert gated(x=None) == NULLP
+    assert gated(h=None) == NULLP
+    assert gated(gate=None) == NULLP
+    assert gated(xd=7) == DTYPE
+    assert gated(xd=BF16, hd=F32) == DTYPE
+    assert gated(rows=-1) == SHAPE
+    assert gated(hidden=0) == SHAPE
+    assert gated(hidden=252) == SHAPE  # not a multiple of 8
+    assert gated(rpg=0) == SHAPE
+    assert gated(x=P(0x10000008)) == MISAL
+    assert gated(xs=260) == STRIDE
+    assert gated(xs=128) == STRIDE  # rows overlap
+    assert gated(h=P(0x10000000 + 512)) == ALIAS  # h overlaps x
+    assert gated(rows=2 ** 31) == UNSUP
+    assert gated(rpg=5, gs=12) == STRIDE  # two groups, stride not a vector multiple
+    assert gated(gate=P(0x10000000 + 64)) == ALIAS
+
+
+# --- SwiGLU -----------------------------------------------------------------------------
+
+def swiglu(out=A(0), os_=64, a=A(1), as_=128, b=P(0x20000000 + 128), bs=128, dt=BF16, rows=10,
+           inner=64):
+    return L.h3f_swiglu(out, os_, a, as_, b, bs, dt, rows, inner, None)
+
+
+def test_swiglu_validation():
+    assert swiglu(out=None, rows=0) == OK
+    assert swiglu(out=None) == NULLP
+    assert swiglu(b=None) == NULLP
+    assert swiglu(dt=3) == DTYPE
+    assert swiglu(inner=60) == SHAPE
+    assert swiglu(inner=0) == SHAPE
+    assert swiglu(a=P(0x20000004)) == MISAL
+    assert swiglu(as_=132) == STRIDE
+    assert swiglu(os_=32) == STRIDE
+    assert swiglu(out=P(0x20000000 + 64)) == ALIAS   # out straddles a's row
+    assert swiglu(out=P(0x20000000 + 144), os_=128) == ALIAS  # out shifted inside b's rows
+    assert swiglu(dt=F32, inner=64, out=P(0x20000000 + 8)) == MISAL
+
+
+# --- AdaLN --------------------------------------------------------------------------------
+
+def adaln(y=A(0), yd=BF16, ys=512, x=A(1), xd=BF16, xs=512, sh=A(2), sc=A(3), gs=0, rpg=4,
+          rows=4, hidden=512, eps=1e-6):
+    return L.h3f_adaln_modulate(y, yd, ys, x, xd, xs, sh, sc, gs, rpg, rows, hidden,
+                                ctypes.c_float(eps), None)
+
+
+def test_adaln_validation():
+    assert adaln(x=None, rows=0) == OK
+    assert adaln(sc=None) == NULLP
+    assert adaln(xd=BF16, yd=F32) == DTYPE
+    assert adaln(hidden=516) == SHAPE
+    assert adaln(hidden=16392, xs=16392, ys=16392) == UNSUP
+    assert adaln(xd=F32, yd=F32, hidden=8196, xs=8196, ys=8196) == UNSUP
+    assert adaln(sh=P(0x30000008)) == MISAL
+    assert adaln(ys=500) == STRIDE
+    assert adaln(y=P(0x20000000 + 16)) == ALIAS  # partial overlap with x
+    assert adaln(y=A(1), yd=BF16, xd=BF16, ys=520) == ALIAS  # same base, other stride
+    assert adaln(y=A(2)) == ALIAS  # y over shift
+
+
+# --- fused gated + AdaLN -----------------------------------------------------------------------
+
+def fused(x=A(0), xd=BF16, xs=512, h=A(1), hd=BF16, hs=512, g=A(2), sh=A(3), sc=A(4), gs=0,
+          rpg=4, y=A(5), yd=BF16, ys=512, rows=4, hidden=512):
+    return L.h3f_gated_residual_adaln(x, xd, xs, h, hd, hs, g, sh, sc, gs, rpg, y, yd, ys, rows,
+                                      hidden, ctypes.c_float(1e-6), None)
+
+
+def test_fused_validation():
+    assert fused(y=None, rows=0) == OK
+    assert fused(y=None) == NULLP
+    assert fused(xd=BF16, hd=F32) == DTYPE
+    assert fused(xd=BF16, yd=F32) == DTYPE
+    assert fused(y=A(0)) == ALIAS  # y may not alias x in the fused form
+    assert fused(y=A(1)) == ALIAS
+    assert fused(hidden=20000, xs=20000, hs=20000, ys=20000) == UNSUP
+
+
+# --- QK RMSNorm + RoPE -------------------------------------------------------------------------
+
+def rope(**kw):
+    r = h3.make_rope(31, 48, 84, 128, (32, 48, 48))
+    for k, v in kw.items():
+        setattr(r, k, v)
+    return r
+
+
+def qk(qo=A(0), qors=5120, qohs=128, ko=A(1), kors=5120, kohs=128, q=A(2), qrs=5120, qhs=128,
+       k=A(3), krs=5120, khs=128, qw=A(4), kw=A(5), dt=BF16, rows=10, heads=40, hd=128, r=None):
+    r = rope() if r is None else r
+    return L.h3f_qk_rmsnorm_rope3d(qo, qors, qohs, ko, kors, kohs, q, qrs, qhs, k, krs, khs, qw, kw,
+                                   dt, rows, heads, hd, ctypes.c_float(1e-6), ctypes.byref(r),
+                                   None)
+
+
+def test_qk_validation():
+    assert qk(q=None, rows=0) == OK
+    assert qk(kw=None) == NULLP
+    assert L.h3f_qk_rmsnorm_rope3d(A(0), 5120, 128, A(1), 5120, 128, A(2), 5120, 128, A(3), 5120,
+                                   128, A(4), A(5), BF16, 10, 40, 128, ctypes.c_float(1e-6), None,
+                                   None) == NULLP
+    assert qk(dt=5) == DTYPE
+    assert qk(hd=124) == SHAPE  # not a multiple of 8
+    assert qk(hd=120) == UNSUP  # 120 / 8 = 15 lanes: not a power of two
+    assert qk(hd=96, qohs=96, kohs=96, qhs=96, khs=96) == UNSUP
+    assert qk(hd=1024, r=rope(d_t=256, d_h=384, d_w=384)) == UNSUP
+    assert qk(r=rope(d_t=30, d_h=50, d_w=48)) == SHAPE  # chunk not a multiple of 8
+    assert qk(r=rope(d_t=32, d_h=48, d_w=40)) == SHAPE  # does not sum to head_dim
+    assert qk(r=rope(pairing=2)) == UNSUP
+    assert qk(r=rope(pairing=1, d_t=40, d_h=40, d_w=48)) == UNSUP  # half split needs 16 | d_c
+    assert qk(r=rope(theta=0.0)) == SHAPE
+    assert qk(r=rope(T=0)) == SHAPE
+    assert qk(r=rope(token_offset=-1)) == SHAPE
+    assert qk(q=P(0x30000002)) == MISAL
+    assert qk(qhs=100) == STRIDE  # heads overlap
+    assert qk(qrs=5000) == STRIDE  # rows overlap
+    assert qk(qhs=132) == STRIDE  # not a vector multiple
+    assert qk(qo=A(3)) == ALIAS  # q_out over k
+    assert qk(ko=A(0)) == ALIAS  # k_out over q_out
+    assert qk(qo=A(2), qohs=256, qors=20480, qhs=128, qrs=20480) == ALIAS  # same base, head strides differ
+    assert qk(qo=A(4)) == ALIAS  # over a weight
+
+
+def test_qk_valid_split_is_not_called():
+    # a valid argument set would launch; make sure the helper above never does by keeping
+    # one invalid field in every call (this test documents the convention)
+    assert qk(r=rope(d_t=32, d_h=40, d_w=56), dt=9) == DTYPE
+
+
+# --- positions, stream copy ---------------------------------------------------------------------
+
+def test_positions_and_copy_validation():
+    r = rope()
+    assert L.h3f_rope3d_positions(None, 0, ctypes.byref(r), None) == OK
+    assert L.h3f_rope3d_positions(None, 5, ctypes.byref(r), None) == NULLP
+    assert L.h3f_rope3d_positions(A(0), 5, None, None) == NULLP
+    assert L.h3f_rope3d_positions(P(0x10000002), 5, ctypes.byref(r), None) == MISAL
+    bad = rope(H=0)
+    assert L.h3f_rope3d_positions(A(0), 5, ctypes.byref(bad), None) == SHAPE
+    assert L.h3f_rope3d_positions(A(0), -5, ctypes.byref(r), None) == SHAPE
+    assert L.h3f_stream_copy(A(0), A(1), 0, None) == OK
+    assert L.h3f_stream_copy(None, A(1), 16, None) == NULLP
+    assert L.h3f_stream_copy(A(0), A(1), 17, None) == SHAPE
+    assert L.h3f_stream_copy(A(0), P(0x10000000 + 32), 64, None) == ALIAS
+    assert L.h3f_stream_copy(A(0), P(0x20000008), 64, None) == MISAL
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        h3.h3f_gated_residual(x, x, x[0])

@@ -1,0 +1,303 @@
+"""Python binding of libh3fused (see include/h3fused.h): fused, memory-bound
+per-token DiT operators as hand-written HIP kernels for gfx950 (MI355X).
+
+Argument marshalling only.  Each function takes torch tensors that live on the
+GPU (torch provides device memory and the current stream), passes their
+pointers, strides and types to the C entry point of the same name, and raises
+H3FError when the library rejects the call.  Every step of the computation runs
+in the HIP kernels; there is no fallback of any kind: without the built library
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libh3fused.so")
+
+H3F_F32 = 0
+H3F_BF16 = 1
+H3F_ROPE_INTERLEAVED = 0
+H3F_ROPE_HALF_SPLIT = 1
+
+STATUS = {
+    0: "H3F_OK", 1: "H3F_ERR_NULL_POINTER", 2: "H3F_ERR_BAD_SHAPE", 3: "H3F_ERR_BAD_STRIDE",
+    4: "H3F_ERR_MISALIGNED", 5: "H3F_ERR_BAD_DTYPE", 6: "H3F_ERR_ALIASING", 7: "H3F_ERR_LAUNCH",
+    8: "H3F_ERR_UNSUPPORTED",
+}
+
+EXPORTS = [
+    "h3f_abi_version", "h3f_status_string", "h3f_rope3d_positions", "h3f_adaln_modulate",
+    "h3f_gated_residual", "h3f_swiglu", "h3f_qk_rmsnorm_rope3d", "h3f_gated_residual_adaln",
+    "h3f_stream_copy",
+]
+
+
+class H3FError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        msg = lib().h3f_status_string(status).decode()
+        super().__init__(f"{fn}: {self.name} ({msg})")
+
+
+class Rope3D(ctypes.Structure):
+    """Mirror of h3f_rope3d_t."""
+    _fields_ = [
+        ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("n_audio", ctypes.c_int32), ("d_t", ctypes.c_int32), ("d_h", ctypes.c_int32),
+        ("d_w", ctypes.c_int32), ("pairing", ctypes.c_int32), ("theta", ctypes.c_double),
+        ("token_offset", ctypes.c_int64), ("positions", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libh3fused.so (ctypes), with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"libh3fused.so is not built ({LIB_PATH}); run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32, f, st = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                              ctypes.c_int)
+        L.h3f_abi_version.restype = ctypes.c_int
+        L.h3f_status_string.argtypes = [st]
+        L.h3f_status_string.restype = ctypes.c_char_p
+        L.h3f_rope3d_positions.argtypes = [p, i64, ctypes.POINTER(Rope3D), p]
+        L.h3f_adaln_modulate.argtypes = [p, st, i64, p, st, i64, p, p, i64, i64, i64, i64, f, p]
+        L.h3f_gated_residual.argtypes = [p, st, i64, p, st, i64, p, i64, i64, i64, i64, p]
+        L.h3f_swiglu.argtypes = [p, i64, p, i64, p, i64, st, i64, i64, p]
+        L.h3f_qk_rmsnorm_rope3d.argtypes = [p, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64,
+                                            p, p, st, i64, i32, i32, f, ctypes.POINTER(Rope3D), p]
+        L.h3f_gated_residual_adaln.argtypes = [p, st, i64, p, st, i64, p, p, p, i64, i64, p, st,
+                                               i64, i64, i64, f, p]
+        L.h3f_stream_copy.argtypes = [p, p, i64, p]
+        for name in EXPORTS[2:]:
+            getattr(L, name).restype = st
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().h3f_abi_version()
+
+
+# ---------------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------------
+
+def _dtype(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return H3F_F32
+    if t.dtype == torch.bfloat16:
+        return H3F_BF16
+    raise TypeError(f"libh3fused takes float32 or bfloat16 tensors, got {t.dtype}")
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("libh3fused operates on GPU tensors only")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors of a call must be on one device")
+    return dev
+
+
+def _stream(dev, stream):
+    import torch
+
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn, status):
+    if status != 0:
+        raise H3FError(fn, status)
+
+
+def _rows2d(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name}: expected a 2-D tensor with unit inner stride")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _mod(v, hidden, name):
+    """Modulation vector(s): [hidden] or [groups, hidden] -> (groups, group stride)."""
+    if v.dim() == 1:
+        v2 = v.view(1, -1)
+    else:
+        v2 = v
+    if v2.dim() != 2 or v2.shape[1] != hidden or v2.stride(1) != 1:
+        raise ValueError(f"{name}: expected [hidden] or [groups, hidden] with unit inner stride")
+    return v2.shape[0], v2.stride(0)
+
+
+def _rows_per_group(rows, groups, rows_per_group):
+    if rows_per_group is not None:
+        return int(rows_per_group)
+    if groups == 1:
+        return max(rows, 1)
+    if rows % groups:
+        raise ValueError("rows_per_group is needed when rows is not a multiple of the group count")
+    return rows // groups
+
+
+# ---------------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------------
+
+def h3f_rope3d_positions(pos, rope: Rope3D, stream=None):
+    """pos: int32 [rows, 3] GPU tensor, filled with (t, h, w) of each row."""
+    import torch
+
+    if pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[1] != 3 or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int32 [rows, 3] tensor")
+    dev = _dev(pos)
+    _check("h3f_rope3d_positions", lib().h3f_rope3d_positions(
+        _ptr(pos), pos.shape[0], ctypes.byref(rope), _stream(dev, stream)))
+    return pos
+
+
+def h3f_adaln_modulate(y, x, shift, scale, eps: float = 1e-6, rows_per_group=None, stream=None):
+    """y[r] = LN(x[r]) * (1 + scale[g]) + shift[g]; y may be x itself."""
+    dev = _dev(y, x, shift, scale)
+    rows, hidden, xs = _rows2d(x, "x")
+    yr, yh, ys = _rows2d(y, "y")
+    if (yr, yh) != (rows, hidden):
+        raise ValueError("y and x shapes differ")
+    groups, gs = _mod(shift, hidden, "shift")
+    g2, gs2 = _mod(scale, hidden, "scale")
+    if (groups, gs) != (g2, gs2):
+        raise ValueError("shift and scale must share shape and strides")
+    rpg = _rows_per_group(rows, groups, rows_per_group)
+    _check("h3f_adaln_modulate", lib().h3f_adaln_modulate(
+        _ptr(y), _dtype(y), ys, _ptr(x), _dtype(x), xs, _ptr(shift), _ptr(scale), gs, rpg, rows,
+        hidden, eps, _stream(dev, stream)))
+    return y
+
+
+def h3f_gated_residual(x, h, gate, rows_per_group=None, stream=None):
+    """x[r] += gate[g] * h[r], in place."""
+    dev = _dev(x, h, gate)
+    rows, hidden, xs = _rows2d(x, "x")
+    hr, hh, hs = _rows2d(h, "h")
+    if (hr, hh) != (rows, hidden):
+        raise ValueError("h and x shapes differ")
+    groups, gs = _mod(gate, hidden, "gate")
+    rpg = _rows_per_group(rows, groups, rows_per_group)
+    _check("h3f_gated_residual", lib().h3f_gated_residual(
+        _ptr(x), _dtype(x), xs, _ptr(h), _dtype(h), hs, _ptr(gate), gs, rpg, rows, hidden,
+        _stream(dev, stream)))
+    return x
+
+
+def h3f_swiglu(out, a, b=None, stream=None):
+    """out = silu(a) * b.  With b None, `a` is the packed [rows, 2*inner] gate/up
+    tensor whose first half is the gate and second half the up projection."""
+    if b is None:
+        inner2 = a.shape[-1]
+        if inner2 % 2:
+            raise ValueError("packed gate/up width must be even")
+        a, b = a[:, : inner2 // 2], a[:, inner2 // 2:]
+    dev = _dev(out, a, b)
+    rows, inner, os_ = _rows2d(out, "out")
+    ar, ai, as_ = _rows2d(a, "a")
+    br, bi, bs = _rows2d(b, "b")
+    if (ar, ai) != (rows, inner) or (br, bi) != (rows, inner):
+        raise ValueError("out, a, b shapes differ")
+    if not (out.dtype == a.dtype == b.dtype):
+        raise TypeError("out, a, b must share a dtype")
+    _check("h3f_swiglu", lib().h3f_swiglu(
+        _ptr(out), os_, _ptr(a), as_, _ptr(b), bs, _dtype(out), rows, inner,
+        _stream(dev, stream)))
+    return out
+
+
+def make_rope(T, H, W, n_audio, split, theta=10000.0, token_offset=0, positions=None,
+              pairing=H3F_ROPE_INTERLEAVED) -> Rope3D:
+    r = Rope3D()
+    r.T, r.H, r.W, r.n_audio = int(T), int(H), int(W), int(n_audio)
+    r.d_t, r.d_h, r.d_w = (int(s) for s in split)
+    r.pairing = int(pairing)
+    r.theta = float(theta)
+    r.token_offset = int(token_offset)
+    r.positions = None if positions is None else positions.data_ptr()
+    return r
+
+
+def _heads3d(t, name):
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name}: expected [rows, heads, head_dim] with unit inner stride")
+    return t.shape, t.stride(0), t.stride(1)
+
+
+def h3f_qk_rmsnorm_rope3d(q_out, k_out, q, k, q_weight, k_weight, rope: Rope3D,
+                          eps: float = 1e-6, stream=None):
+    """Per-head RMSNorm of q and k, then 3D RoPE.  Tensors are [rows, heads, head_dim]
+    views (any row / head strides); q_out / k_out may be q / k themselves."""
+    dev = _dev(q_out, k_out, q, k, q_weight, k_weight)
+    shp, qrs, qhs = _heads3d(q, "q")
+    kshp, krs, khs = _heads3d(k, "k")
+    qoshp, qors, qohs = _heads3d(q_out, "q_out")
+    koshp, kors, kohs = _heads3d(k_out, "k_out")
+    if not (shp == kshp == qoshp == koshp):
+        raise ValueError("q, k, q_out, k_out shapes differ")
+    rows, heads, head_dim = shp
+    for w, n in ((q_weight, "q_weight"), (k_weight, "k_weight")):
+        if w.numel() != head_dim or not w.is_contiguous():
+            raise ValueError(f"{n}: expected a contiguous [head_dim] tensor")
+    dt = _dtype(q)
+    for t in (k, q_out, k_out, q_weight, k_weight):
+        if _dtype(t) != dt:
+            raise TypeError("all qk tensors must share one dtype")
+    _check("h3f_qk_rmsnorm_rope3d", lib().h3f_qk_rmsnorm_rope3d(
+        _ptr(q_out), qors, qohs, _ptr(k_out), kors, kohs, _ptr(q), qrs, qhs, _ptr(k), krs, khs,
+        _ptr(q_weight), _ptr(k_weight), dt, rows, heads, head_dim, eps, ctypes.byref(rope),
+        _stream(dev, stream)))
+    return q_out, k_out
+
+
+def h3f_gated_residual_adaln(x, h, gate, shift, scale, y, eps: float = 1e-6,
+                             rows_per_group=None, stream=None):
+    """x[r] += gate[g] * h[r] (in place), then y[r] = AdaLN(x[r]; shift[g], scale[g])."""
+    dev = _dev(x, h, gate, shift, scale, y)
+    rows, hidden, xs = _rows2d(x, "x")
+    hr, hh, hs = _rows2d(h, "h")
+    yr, yh, ys = _rows2d(y, "y")
+    if (hr, hh) != (rows, hidden) or (yr, yh) != (rows, hidden):
+        raise ValueError("x, h, y shapes differ")
+    shapes = [_mod(v, hidden, n) for v, n in ((gate, "gate"), (shift, "shift"), (scale, "scale"))]
+    if len(set(shapes)) != 1:
+        raise ValueError("gate, shift and scale must share shape and strides")
+    groups, gs = shapes[0]
+    rpg = _rows_per_group(rows, groups, rows_per_group)
+    _check("h3f_gated_residual_adaln", lib().h3f_gated_residual_adaln(
+        _ptr(x), _dtype(x), xs, _ptr(h), _dtype(h), hs, _ptr(gate), _ptr(shift), _ptr(scale), gs,
+        rpg, _ptr(y), _dtype(y), ys, rows, hidden, eps, _stream(dev, stream)))
+    return x, y
+
+
+def h3f_stream_copy(dst, src, stream=None):
+    """Byte copy src -> dst (measurement helper); both contiguous, same byte size."""
+    dev = _dev(dst, src)
+    nb = src.numel() * src.element_size()
+    if not (dst.is_contiguous() and src.is_contiguous()) or dst.numel() * dst.element_size() != nb:
+        raise ValueError("dst and src must be contiguous with equal byte sizes")
+    _check("h3f_stream_copy", lib().h3f_stream_copy(_ptr(dst), _ptr(src), nb,
+                                                    _stream(dev, stream)))
+    return dst

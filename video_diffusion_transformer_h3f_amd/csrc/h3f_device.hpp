@@ -1,0 +1,156 @@
+// h3f_device.hpp -- device-side building blocks shared by the libh3fused kernels:
+// 16-byte vector memory access, bf16 <-> fp32 conversion, and DPP / swizzle
+// reductions inside groups of lanes of a 64-wide wavefront (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3f {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// 16-byte loads / stores.  The non-temporal forms mark streams that are
+// touched once, so they do not displace reused data (modulation vectors,
+// norm weights) from the caches.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Vec<T, N>: N consecutive elements of storage type T (float or __bf16) held
+// as raw 16-byte quads; widened to fp32 on use, narrowed with one
+// round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950) on store.
+// ---------------------------------------------------------------------------
+template <typename T, int N>
+struct Vec {
+    static constexpr int kQuads = N * (int)sizeof(T) / 16;
+    static_assert(kQuads >= 1 && N * (int)sizeof(T) % 16 == 0, "vector must be whole 16-byte quads");
+    u32x4 q[kQuads];
+
+    template <bool NT>
+    __device__ __forceinline__ void load(const T* p) {
+#pragma unroll
+        for (int i = 0; i < kQuads; ++i)
+            q[i] = NT ? ld16_nt(p + i * (16 / (int)sizeof(T))) : ld16(p + i * (16 / (int)sizeof(T)));
+    }
+    template <bool NT>
+    __device__ __forceinline__ void store(T* p) const {
+#pragma unroll
+        for (int i = 0; i < kQuads; ++i) {
+            if (NT)
+                st16_nt(p + i * (16 / (int)sizeof(T)), q[i]);
+            else
+                st16(p + i * (16 / (int)sizeof(T)), q[i]);
+        }
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < kQuads; ++i) q[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    __device__ __forceinline__ void to_float(float (&f)[N]) const {
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int i = 0; i < kQuads; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[4 * i + j] = __uint_as_float(q[i][j]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kQuads; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f[8 * i + 2 * j] = __uint_as_float(q[i][j] << 16);
+                    f[8 * i + 2 * j + 1] = __uint_as_float(q[i][j] & 0xffff0000u);
+                }
+        }
+    }
+    __device__ __forceinline__ void from_float(const float (&f)[N]) {
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int i = 0; i < kQuads; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) q[i][j] = __float_as_uint(f[4 * i + j]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kQuads; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x2 v = {f[8 * i + 2 * j], f[8 * i + 2 * j + 1]};
+                    q[i][j] = __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+                }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Reductions over aligned groups of L lanes (L = 1, 2, ..., 64).  Every lane of
+// a group ends with the same, bit-identical sum (each step adds a value and its
+// mirror, and fp32 addition is commutative).  Steps:
+//   xor 1, xor 2  : DPP quad_perm
+//   8-lane       : DPP row_half_mirror (lane i <- 7 - i within 8)
+//   16-lane      : DPP row_mirror      (lane i <- 15 - i within 16)
+//   32-lane      : ds_swizzle, xor 16 within 32
+//   64-lane      : ds_bpermute, xor 32
+// The caller keeps all 64 lanes active at the call.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(L == 1 || L == 2 || L == 4 || L == 8 || L == 16 || L == 32 || L == 64, "L");
+    if constexpr (L >= 2) v += dpp_mov<0xB1>(v);   // quad_perm(1,0,3,2)
+    if constexpr (L >= 4) v += dpp_mov<0x4E>(v);   // quad_perm(2,3,0,1)
+    if constexpr (L >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+    if constexpr (L >= 16) v += dpp_mov<0x140>(v); // row_mirror
+    if constexpr (L >= 32)
+        v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // xor 16
+    if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Sum over the whole wavefront, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = group_sum<32>(v);
+    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    return lo + hi;
+}
+
+// ---------------------------------------------------------------------------
+// Unsigned 32-bit division by a run-time invariant divisor d >= 1 for
+// dividends n < 2^31: q = (mulhi(n, m) + n) >> s with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1 (Granlund & Montgomery, PLDI 1994, sec. 4).
+// ---------------------------------------------------------------------------
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+__host__ inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    uint32_t s = 0;
+    while ((uint64_t(1) << s) < d) ++s;
+    f.s = s;
+    f.m = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1);
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+    return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+}  // namespace h3f

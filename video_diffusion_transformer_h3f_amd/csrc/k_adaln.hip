@@ -1,0 +1,303 @@
+// k_adaln.hip -- AdaLN modulate and the fused gated residual + AdaLN.
+//
+// Design (gfx950): one 64-wide wavefront owns one token row at a time and
+// keeps the whole row in VGPRs (NV chunks of VEC elements per lane; hidden
+// 5120 bf16 is 10 x 16-byte quads per lane).  x is read from HBM exactly once:
+// the mean and then the centred second moment are reduced from registers
+// (DPP / swizzle inside the wave, no LDS, no barrier), and the normalised,
+// modulated row is written once.  The fused variant first applies the gated
+// residual to the registers, rounds to x's storage type, writes x back, and
+// normalises that stored value -- so it reads x once instead of twice.
+// Modulation vectors are loaded with ordinary (cached) loads: every row of a
+// group re-reads them from L1/L2, never from HBM.
+#include <hip/hip_runtime.h>
+
+#include "h3f_device.hpp"
+#include "h3f_validate.hpp"
+
+namespace h3f {
+namespace {
+
+constexpr int kWaves = 4;  // wavefronts per workgroup
+constexpr int kRowsPerWave = 2;
+
+struct AdalnArgs {
+    void* y;
+    int64_t y_rs;
+    void* x;
+    int64_t x_rs;
+    const void* h;
+    int64_t h_rs;
+    const void* gate;
+    const void* shift;
+    const void* scale;
+    int64_t mod_gs;
+    FastDiv div_group;
+    int64_t rows;
+    int32_t nvec;  // hidden / VEC
+    float inv_hidden;
+    float eps;
+};
+
+template <typename TX, typename TY, typename TH, int VEC, int NV, bool FUSED>
+__global__ void __launch_bounds__(kWaves * 64) adaln_kernel(AdalnArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    TX* __restrict__ x = static_cast<TX*>(a.x);
+    TY* __restrict__ y = static_cast<TY*>(a.y);
+    const TX* __restrict__ shift = static_cast<const TX*>(a.shift);
+    const TX* __restrict__ scale = static_cast<const TX*>(a.scale);
+
+    for (int64_t row = wave; row < a.rows; row += nwaves) {
+        const uint32_t grp = fdiv((uint32_t)row, a.div_group);
+        TX* xr = x + row * a.x_rs;
+        float v[NV][VEC];
+        bool valid[NV];
+        {
+            Vec<TX, VEC> xv[NV];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int c = i * 64 + lane;
+                valid[i] = c < a.nvec;
+                if (valid[i])
+                    xv[i].template load<true>(xr + c * VEC);
+                else
+                    xv[i].zero();
+            }
+            if constexpr (FUSED) {
+                const TH* hr = static_cast<const TH*>(a.h) + row * a.h_rs;
+                const TX* gr = static_cast<const TX*>(a.gate) + (int64_t)grp * a.mod_gs;
+                Vec<TH, VEC> hv[NV];
+                Vec<TX, VEC> gv[NV];
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const int c = i * 64 + lane;
+                    if (valid[i]) {
+                        hv[i].template load<true>(hr + c * VEC);
+                        gv[i].template load<false>(gr + c * VEC);
+                    } else {
+                        hv[i].zero();
+                        gv[i].zero();
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    float xf[VEC], hf[VEC], gf[VEC];
+                    xv[i].to_float(xf);
+                    hv[i].to_float(hf);
+                    gv[i].to_float(gf);
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) xf[j] = __builtin_fmaf(gf[j], hf[j], xf[j]);
+                    xv[i].from_float(xf);  // round to x's storage type
+                    if (valid[i]) xv[i].template store<true>(xr + (i * 64 + lane) * VEC);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i) xv[i].to_float(v[i]);
+        }
+
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) s += v[i][j];
+        const float mean = wave_sum(s) * a.inv_hidden;
+
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if (!valid[i]) continue;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const float d = v[i][j] - mean;
+                ss = __builtin_fmaf(d, d, ss);
+            }
+        }
+        const float var = wave_sum(ss) * a.inv_hidden;
+        const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
+
+        const TX* shr = shift + (int64_t)grp * a.mod_gs;
+        const TX* scr = scale + (int64_t)grp * a.mod_gs;
+        TY* yr = y + row * a.y_rs;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if (!valid[i]) continue;
+            const int c = (i * 64 + lane) * VEC;
+            Vec<TX, VEC> shv, scv;
+            shv.template load<false>(shr + c);
+            scv.template load<false>(scr + c);
+            float sh[VEC], sc[VEC], o[VEC];
+            shv.to_float(sh);
+            scv.to_float(sc);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                o[j] = __builtin_fmaf((v[i][j] - mean) * rstd, 1.0f + sc[j], sh[j]);
+            Vec<TY, VEC> ov;
+            ov.from_float(o);
+            ov.template store<true>(yr + c);
+        }
+    }
+}
+
+
+template <typename TX, typename TY, typename TH, int VEC, bool FUSED, int NV>
+hipError_t launch_nv(const AdalnArgs& a, hipStream_t st) {
+    int64_t blocks = (a.rows + kWaves * kRowsPerWave - 1) / (kWaves * kRowsPerWave);
+    if (blocks > 0x7fffffff) blocks = 0x7fffffff;
+    hipLaunchKernelGGL((adaln_kernel<TX, TY, TH, VEC, NV, FUSED>), dim3((unsigned)blocks),
+                       dim3(kWaves * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename TX, typename TY, typename TH, int VEC, bool FUSED>
+h3f_status_t dispatch(const AdalnArgs& a, int max_nv, hipStream_t st) {
+    const int need = (a.nvec + 63) / 64;
+    hipError_t e = hipErrorInvalidValue;
+#define H3F_NV_CASE(N)                                                   \
+    else if (need <= N && N <= max_nv) e = launch_nv<TX, TY, TH, VEC, FUSED, N>(a, st);
+    if (false) {
+    }
+    H3F_NV_CASE(1) H3F_NV_CASE(2) H3F_NV_CASE(3) H3F_NV_CASE(4) H3F_NV_CASE(5) H3F_NV_CASE(6)
+    H3F_NV_CASE(8) H3F_NV_CASE(10) H3F_NV_CASE(12) H3F_NV_CASE(16)
+    H3F_NV_CASE(20) H3F_NV_CASE(24) H3F_NV_CASE(32)
+    else return H3F_ERR_UNSUPPORTED;
+#undef H3F_NV_CASE
+    return e == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
+}
+
+// Largest hidden size held in registers: 32 chunks of 8 bf16, 16 chunks of 8
+// fp32 (mixed) or 32 chunks of 4 fp32.
+inline int64_t max_hidden(h3f_dtype_t x_dtype) { return x_dtype == H3F_BF16 ? 16384 : 8192; }
+inline int max_nv_for(h3f_dtype_t x_dtype, int V) {
+    return x_dtype == H3F_BF16 ? 32 : (V == 8 ? 16 : 32);
+}
+
+h3f_status_t check_mod(const void* p, int64_t groups, int64_t gs, int64_t hidden, int V) {
+    if (!aligned16(p)) return H3F_ERR_MISALIGNED;
+    if (groups > 1 && gs % V) return H3F_ERR_BAD_STRIDE;
+    (void)hidden;
+    return H3F_OK;
+}
+
+}  // namespace
+}  // namespace h3f
+
+using namespace h3f;
+
+extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t y_row_stride,
+                                           const void* x, h3f_dtype_t x_dtype,
+                                           int64_t x_row_stride, const void* shift,
+                                           const void* scale, int64_t mod_group_stride,
+                                           int64_t rows_per_group, int64_t rows, int64_t hidden,
+                                           float eps, void* stream) {
+    if (rows == 0) return H3F_OK;
+    if (!y || !x || !shift || !scale) return H3F_ERR_NULL_POINTER;
+    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return H3F_ERR_BAD_DTYPE;
+    if (x_dtype == H3F_BF16 && y_dtype == H3F_F32) return H3F_ERR_BAD_DTYPE;
+    if (rows < 0 || hidden <= 0 || rows_per_group < 1) return H3F_ERR_BAD_SHAPE;
+    const int V = vec_width(x_dtype == H3F_BF16 || y_dtype == H3F_BF16);
+    if (hidden % V) return H3F_ERR_BAD_SHAPE;
+    if (hidden > max_hidden(x_dtype) || rows > 0x7fffffff) return H3F_ERR_UNSUPPORTED;
+    if (!aligned16(y) || !aligned16(x)) return H3F_ERR_MISALIGNED;
+    const int64_t groups = groups_for(rows, rows_per_group);
+    h3f_status_t s;
+    if ((s = check_mod(shift, groups, mod_group_stride, hidden, V)) != H3F_OK) return s;
+    if ((s = check_mod(scale, groups, mod_group_stride, hidden, V)) != H3F_OK) return s;
+    if (rows > 1 && (x_row_stride % V || y_row_stride % V)) return H3F_ERR_BAD_STRIDE;
+    const int ex = dtype_bytes(x_dtype), ey = dtype_bytes(y_dtype);
+    const Region rx = region2d(x, rows, x_row_stride, hidden, ex);
+    const Region ry = region2d(y, rows, y_row_stride, hidden, ey);
+    const Region rsh = region2d(shift, groups, mod_group_stride, hidden, ex);
+    const Region rsc = region2d(scale, groups, mod_group_stride, hidden, ex);
+    if (!rows_separate(rx) || !rows_separate(ry) || !rows_separate(rsh) || !rows_separate(rsc))
+        return H3F_ERR_BAD_STRIDE;
+    if (!alias_ok(ry, rx, x_dtype == y_dtype) || !disjoint(ry, rsh) || !disjoint(ry, rsc))
+        return H3F_ERR_ALIASING;
+
+    AdalnArgs a{};
+    a.y = y;
+    a.y_rs = rows > 1 ? y_row_stride : hidden;
+    a.x = const_cast<void*>(x);
+    a.x_rs = rows > 1 ? x_row_stride : hidden;
+    a.shift = shift;
+    a.scale = scale;
+    a.mod_gs = groups > 1 ? mod_group_stride : 0;
+    a.div_group = make_fastdiv((uint32_t)(rows_per_group > rows ? rows : rows_per_group));
+    a.rows = rows;
+    a.nvec = (int32_t)(hidden / V);
+    a.inv_hidden = 1.0f / (float)hidden;
+    a.eps = eps;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int mnv = max_nv_for(x_dtype, V);
+    if (x_dtype == H3F_F32 && y_dtype == H3F_F32)
+        return dispatch<float, float, float, 4, false>(a, mnv, st);
+    if (x_dtype == H3F_BF16)
+        return dispatch<__bf16, __bf16, __bf16, 8, false>(a, mnv, st);
+    return dispatch<float, __bf16, float, 8, false>(a, mnv, st);
+}
+
+extern "C" h3f_status_t h3f_gated_residual_adaln(
+    void* x, h3f_dtype_t x_dtype, int64_t x_row_stride, const void* h, h3f_dtype_t h_dtype,
+    int64_t h_row_stride, const void* gate, const void* shift, const void* scale,
+    int64_t mod_group_stride, int64_t rows_per_group, void* y, h3f_dtype_t y_dtype,
+    int64_t y_row_stride, int64_t rows, int64_t hidden, float eps, void* stream) {
+    if (rows == 0) return H3F_OK;
+    if (!x || !h || !gate || !shift || !scale || !y) return H3F_ERR_NULL_POINTER;
+    if (!dtype_ok(x_dtype) || !dtype_ok(h_dtype) || !dtype_ok(y_dtype)) return H3F_ERR_BAD_DTYPE;
+    if (x_dtype == H3F_BF16 && (h_dtype == H3F_F32 || y_dtype == H3F_F32))
+        return H3F_ERR_BAD_DTYPE;
+    if (rows < 0 || hidden <= 0 || rows_per_group < 1) return H3F_ERR_BAD_SHAPE;
+    const int V = vec_width(x_dtype == H3F_BF16 || h_dtype == H3F_BF16 || y_dtype == H3F_BF16);
+    if (hidden % V) return H3F_ERR_BAD_SHAPE;
+    if (hidden > max_hidden(x_dtype) || rows > 0x7fffffff) return H3F_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(h) || !aligned16(y)) return H3F_ERR_MISALIGNED;
+    const int64_t groups = groups_for(rows, rows_per_group);
+    h3f_status_t s;
+    if ((s = check_mod(gate, groups, mod_group_stride, hidden, V)) != H3F_OK) return s;
+    if ((s = check_mod(shift, groups, mod_group_stride, hidden, V)) != H3F_OK) return s;
+    if ((s = check_mod(scale, groups, mod_group_stride, hidden, V)) != H3F_OK) return s;
+    if (rows > 1 && (x_row_stride % V || h_row_stride % V || y_row_stride % V))
+        return H3F_ERR_BAD_STRIDE;
+    const int ex = dtype_bytes(x_dtype), eh = dtype_bytes(h_dtype), ey = dtype_bytes(y_dtype);
+    const Region rx = region2d(x, rows, x_row_stride, hidden, ex);
+    const Region rh = region2d(h, rows, h_row_stride, hidden, eh);
+    const Region ry = region2d(y, rows, y_row_stride, hidden, ey);
+    const Region rg = region2d(gate, groups, mod_group_stride, hidden, ex);
+    const Region rsh = region2d(shift, groups, mod_group_stride, hidden, ex);
+    const Region rsc = region2d(scale, groups, mod_group_stride, hidden, ex);
+    if (!rows_separate(rx) || !rows_separate(rh) || !rows_separate(ry) || !rows_separate(rg) ||
+        !rows_separate(rsh) || !rows_separate(rsc))
+        return H3F_ERR_BAD_STRIDE;
+    const Region* others_x[] = {&rh, &rg, &rsh, &rsc, &ry};
+    for (const Region* o : others_x)
+        if (!disjoint(rx, *o)) return H3F_ERR_ALIASING;
+    const Region* others_y[] = {&rh, &rg, &rsh, &rsc};
+    for (const Region* o : others_y)
+        if (!disjoint(ry, *o)) return H3F_ERR_ALIASING;
+
+    AdalnArgs a{};
+    a.y = y;
+    a.y_rs = rows > 1 ? y_row_stride : hidden;
+    a.x = x;
+    a.x_rs = rows > 1 ? x_row_stride : hidden;
+    a.h = h;
+    a.h_rs = rows > 1 ? h_row_stride : hidden;
+    a.gate = gate;
+    a.shift = shift;
+    a.scale = scale;
+    a.mod_gs = groups > 1 ? mod_group_stride : 0;
+    a.div_group = make_fastdiv((uint32_t)(rows_per_group > rows ? rows : rows_per_group));
+    a.rows = rows;
+    a.nvec = (int32_t)(hidden / V);
+    a.inv_hidden = 1.0f / (float)hidden;
+    a.eps = eps;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int mnv = max_nv_for(x_dtype, V);
+    if (x_dtype == H3F_BF16) return dispatch<__bf16, __bf16, __bf16, 8, true>(a, mnv, st);
+    if (h_dtype == H3F_F32 && y_dtype == H3F_F32)
+        return dispatch<float, float, float, 4, true>(a, mnv, st);
+    if (h_dtype == H3F_F32) return dispatch<float, __bf16, float, 8, true>(a, mnv, st);
+    if (y_dtype == H3F_F32) return dispatch<float, float, __bf16, 8, true>(a, mnv, st);
+    return dispatch<float, __bf16, __bf16, 8, true>(a, mnv, st);
+}
