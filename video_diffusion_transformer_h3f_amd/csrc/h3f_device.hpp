@@ -29,6 +29,63 @@ __device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
 }
 
 // ---------------------------------------------------------------------------
+// Buffer (MUBUF) access through a wave-uniform resource over [base, base +
+// bytes).  Loads outside the range return 0 and stores outside it are
+// dropped, so a row's ragged tail needs no branch.  The cache-policy bits of
+// gfx950 (sc0 = 1, nt = 2, sc1 = 16) are chosen per stream:
+//   kLoadStream  = nt             streaming read, not kept in L2
+//   kStoreStream = sc0 | sc1 | nt streaming write-through: measured on MI355X
+//                                 as the fastest store form for data that is
+//                                 not re-read (about 3% over nt alone)
+//   kLoadReuse   = 0              cached read (modulation vectors, weights)
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+#ifndef H3F_LOAD_AUX
+#define H3F_LOAD_AUX 2
+#endif
+#ifndef H3F_STORE_AUX
+#define H3F_STORE_AUX 19
+#endif
+constexpr int kLoadStream = H3F_LOAD_AUX;
+constexpr int kStoreStream = H3F_STORE_AUX;
+constexpr int kLoadReuse = 0;
+
+// Data-format word of a raw 32-bit buffer resource on gfx9.
+constexpr int kRsrcFlags = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRsrcFlags);
+}
+
+template <int AUX>
+__device__ __forceinline__ u32x4 buf_ld(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+}
+
+template <int AUX>
+__device__ __forceinline__ void buf_st(rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, AUX);
+}
+
+// Byte count of a resource covering `rows` rows of `row_bytes` bytes spaced
+// `stride_bytes` apart, clamped to what a resource can address.
+__host__ __device__ __forceinline__ uint32_t span_bytes(int64_t rows, int64_t stride_bytes,
+                                                        int64_t row_bytes) {
+    if (rows <= 0) return 0;
+    const int64_t b = (rows - 1) * stride_bytes + row_bytes;
+    return b > 0xFFFFFFF0ll ? 0xFFFFFFF0u : (uint32_t)b;
+}
+
+// Make a wave-uniform value provably uniform (lives in an SGPR).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// ---------------------------------------------------------------------------
 // Vec<T, N>: N consecutive elements of storage type T (float or __bf16) held
 // as raw 16-byte quads; widened to fp32 on use, narrowed with one
 // round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950) on store.
@@ -54,6 +111,17 @@ struct Vec {
             else
                 st16(p + i * (16 / (int)sizeof(T)), q[i]);
         }
+    }
+    // Buffer forms: byte offset of the first element inside the resource.
+    template <int AUX>
+    __device__ __forceinline__ void load_buf(rsrc_t r, uint32_t off) {
+#pragma unroll
+        for (int i = 0; i < kQuads; ++i) q[i] = buf_ld<AUX>(r, off + 16u * i);
+    }
+    template <int AUX>
+    __device__ __forceinline__ void store_buf(rsrc_t r, uint32_t off) const {
+#pragma unroll
+        for (int i = 0; i < kQuads; ++i) buf_st<AUX>(r, off + 16u * i, q[i]);
     }
     __device__ __forceinline__ void zero() {
 #pragma unroll

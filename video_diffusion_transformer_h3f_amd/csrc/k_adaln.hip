@@ -1,15 +1,20 @@
 // k_adaln.hip -- AdaLN modulate and the fused gated residual + AdaLN.
 //
-// Design (gfx950): one 64-wide wavefront owns one token row at a time and
-// keeps the whole row in VGPRs (NV chunks of VEC elements per lane; hidden
-// 5120 bf16 is 10 x 16-byte quads per lane).  x is read from HBM exactly once:
-// the mean and then the centred second moment are reduced from registers
-// (DPP / swizzle inside the wave, no LDS, no barrier), and the normalised,
-// modulated row is written once.  The fused variant first applies the gated
-// residual to the registers, rounds to x's storage type, writes x back, and
-// normalises that stored value -- so it reads x once instead of twice.
-// Modulation vectors are loaded with ordinary (cached) loads: every row of a
-// group re-reads them from L1/L2, never from HBM.
+// Design (gfx950): one 64-wide wavefront owns one token row and keeps the
+// whole row in VGPRs (NV chunks of VEC elements per lane; hidden 5120 bf16 is
+// 10 x 16-byte quads per lane).  x is read from HBM exactly once: the mean and
+// then the centred second moment are reduced from registers (DPP / swizzle
+// inside the wave, no LDS, no barrier), and the normalised, modulated row is
+// written once.  The fused variant first applies the gated residual to the
+// registers, rounds to x's storage type, writes x back, and normalises that
+// stored value -- so it reads x once instead of twice.
+// Modulation vectors: when the whole call uses one group (the usual case: one
+// precomputed AdaLN vector set per sample), each workgroup stages them once
+// in LDS and its wavefronts read them from there; otherwise every row reads
+// its group's vectors through the cache hierarchy (L1/L2, not HBM).
+// Measured on MI355X: one row per wavefront, no grid-stride reuse, is the
+// fastest organisation (multi-wavefront rows pay more in barriers than they
+// gain in finer-grained streaming).
 #include <hip/hip_runtime.h>
 
 #include "h3f_device.hpp"
@@ -18,144 +23,178 @@
 namespace h3f {
 namespace {
 
-constexpr int kWaves = 4;  // wavefronts per workgroup
-constexpr int kRowsPerWave = 2;
+#ifndef H3F_ADALN_WAVES
+#define H3F_ADALN_WAVES 4
+#endif
+constexpr int kWaves = H3F_ADALN_WAVES;  // wavefronts (= rows) per workgroup
 
 struct AdalnArgs {
     void* y;
-    int64_t y_rs;
+    int64_t y_rs;  // bytes
     void* x;
-    int64_t x_rs;
+    int64_t x_rs;  // bytes
     const void* h;
-    int64_t h_rs;
+    int64_t h_rs;  // bytes
     const void* gate;
     const void* shift;
     const void* scale;
-    int64_t mod_gs;
+    int64_t mod_gs;  // bytes
     FastDiv div_group;
     int64_t rows;
     int32_t nvec;  // hidden / VEC
+    int32_t hidden;
     float inv_hidden;
     float eps;
 };
 
-template <typename TX, typename TY, typename TH, int VEC, int NV, bool FUSED>
-__global__ void __launch_bounds__(kWaves * 64) adaln_kernel(AdalnArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
-    TX* __restrict__ x = static_cast<TX*>(a.x);
-    TY* __restrict__ y = static_cast<TY*>(a.y);
-    const TX* __restrict__ shift = static_cast<const TX*>(a.shift);
-    const TX* __restrict__ scale = static_cast<const TX*>(a.scale);
+// Modulation vector chunk c of group grp: from LDS (staged, single group) or memory.
+template <typename TX, int VEC, bool LDSMOD>
+struct ModSource {
+    static constexpr int Q = Vec<TX, VEC>::kQuads;
+    const u32x4* lds;  // [n_vectors][nvec * Q]
+    int32_t nvec;
+    rsrc_t r[3];
+    __device__ __forceinline__ void get(int which, uint32_t c, Vec<TX, VEC>& v) const {
+        if constexpr (LDSMOD) {
+#pragma unroll
+            for (int k = 0; k < Q; ++k) v.q[k] = lds[(which * nvec + c) * Q + k];
+        } else {
+            v.template load_buf<kLoadReuse>(r[which], c * (VEC * sizeof(TX)));
+        }
+    }
+};
 
-    for (int64_t row = wave; row < a.rows; row += nwaves) {
-        const uint32_t grp = fdiv((uint32_t)row, a.div_group);
-        TX* xr = x + row * a.x_rs;
-        float v[NV][VEC];
-        bool valid[NV];
-        {
-            Vec<TX, VEC> xv[NV];
+extern __shared__ u32x4 adaln_lds[];
+
+template <typename TX, typename TY, typename TH, int VEC, int NV, bool FUSED, bool LDSMOD>
+__global__ void __launch_bounds__(kWaves * 64) adaln_kernel(AdalnArgs a) {
+    constexpr int Q = Vec<TX, VEC>::kQuads;
+    constexpr int NMOD = FUSED ? 3 : 2;  // (gate,) shift, scale
+    const int lane = threadIdx.x & 63;
+    const uint32_t xrow_bytes = (uint32_t)a.hidden * sizeof(TX);
+    const void* mods[3] = {a.shift, a.scale, a.gate};
+
+    ModSource<TX, VEC, LDSMOD> ms;
+    ms.nvec = a.nvec;
+    ms.lds = adaln_lds;
+    if constexpr (LDSMOD) {
+        // stage group 0's vectors: NMOD x nvec chunks of Q quads
+        const int per = a.nvec * Q;
+        for (int i = threadIdx.x; i < NMOD * per; i += kWaves * 64) {
+            const int which = i / per;
+            adaln_lds[i] = ld16(static_cast<const char*>(mods[which]) + (size_t)(i - which * per) * 16);
+        }
+        __syncthreads();
+    }
+
+    const int64_t row = uniform64((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6));
+    if (row >= a.rows) return;
+    const uint32_t grp = fdiv((uint32_t)row, a.div_group);
+    if constexpr (!LDSMOD) {
+#pragma unroll
+        for (int m = 0; m < NMOD; ++m)
+            ms.r[m] = make_rsrc(static_cast<const char*>(mods[m]) + grp * a.mod_gs, xrow_bytes);
+    }
+    char* xr = static_cast<char*>(a.x) + row * a.x_rs;
+    const rsrc_t rx = make_rsrc(xr, xrow_bytes);
+    float v[NV][VEC];
+    bool valid[NV];
+    {
+        Vec<TX, VEC> xv[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = i * 64 + lane;
+            valid[i] = c < a.nvec;
+            xv[i].template load_buf<kLoadStream>(rx, (uint32_t)c * (VEC * sizeof(TX)));
+        }
+        if constexpr (FUSED) {
+            const rsrc_t rh = make_rsrc(static_cast<const char*>(a.h) + row * a.h_rs,
+                                        (uint32_t)a.hidden * sizeof(TH));
+            Vec<TH, VEC> hv[NV];
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                hv[i].template load_buf<kLoadStream>(rh, (uint32_t)(i * 64 + lane) * (VEC * sizeof(TH)));
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const int c = i * 64 + lane;
-                valid[i] = c < a.nvec;
-                if (valid[i])
-                    xv[i].template load<true>(xr + c * VEC);
-                else
-                    xv[i].zero();
-            }
-            if constexpr (FUSED) {
-                const TH* hr = static_cast<const TH*>(a.h) + row * a.h_rs;
-                const TX* gr = static_cast<const TX*>(a.gate) + (int64_t)grp * a.mod_gs;
-                Vec<TH, VEC> hv[NV];
-                Vec<TX, VEC> gv[NV];
+                const uint32_t c = i * 64 + lane;
+                Vec<TX, VEC> gv;
+                if (valid[i]) ms.get(2, c, gv); else gv.zero();
+                float xf[VEC], hf[VEC], gf[VEC];
+                xv[i].to_float(xf);
+                hv[i].to_float(hf);
+                gv.to_float(gf);
 #pragma unroll
-                for (int i = 0; i < NV; ++i) {
-                    const int c = i * 64 + lane;
-                    if (valid[i]) {
-                        hv[i].template load<true>(hr + c * VEC);
-                        gv[i].template load<false>(gr + c * VEC);
-                    } else {
-                        hv[i].zero();
-                        gv[i].zero();
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < NV; ++i) {
-                    float xf[VEC], hf[VEC], gf[VEC];
-                    xv[i].to_float(xf);
-                    hv[i].to_float(hf);
-                    gv[i].to_float(gf);
-#pragma unroll
-                    for (int j = 0; j < VEC; ++j) xf[j] = __builtin_fmaf(gf[j], hf[j], xf[j]);
-                    xv[i].from_float(xf);  // round to x's storage type
-                    if (valid[i]) xv[i].template store<true>(xr + (i * 64 + lane) * VEC);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NV; ++i) xv[i].to_float(v[i]);
-        }
-
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) s += v[i][j];
-        const float mean = wave_sum(s) * a.inv_hidden;
-
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            if (!valid[i]) continue;
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                const float d = v[i][j] - mean;
-                ss = __builtin_fmaf(d, d, ss);
+                for (int j = 0; j < VEC; ++j) xf[j] = __builtin_fmaf(gf[j], hf[j], xf[j]);
+                xv[i].from_float(xf);  // round to x's storage type
+                xv[i].template store_buf<kStoreStream>(rx, c * (VEC * sizeof(TX)));
             }
         }
-        const float var = wave_sum(ss) * a.inv_hidden;
-        const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) xv[i].to_float(v[i]);
+    }
 
-        const TX* shr = shift + (int64_t)grp * a.mod_gs;
-        const TX* scr = scale + (int64_t)grp * a.mod_gs;
-        TY* yr = y + row * a.y_rs;
+    float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            if (!valid[i]) continue;
-            const int c = (i * 64 + lane) * VEC;
-            Vec<TX, VEC> shv, scv;
-            shv.template load<false>(shr + c);
-            scv.template load<false>(scr + c);
-            float sh[VEC], sc[VEC], o[VEC];
-            shv.to_float(sh);
-            scv.to_float(sc);
+    for (int i = 0; i < NV; ++i)
 #pragma unroll
-            for (int j = 0; j < VEC; ++j)
-                o[j] = __builtin_fmaf((v[i][j] - mean) * rstd, 1.0f + sc[j], sh[j]);
-            Vec<TY, VEC> ov;
-            ov.from_float(o);
-            ov.template store<true>(yr + c);
+        for (int j = 0; j < VEC; ++j) s += v[i][j];
+    const float mean = wave_sum(s) * a.inv_hidden;
+
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        if (!valid[i]) continue;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            const float d = v[i][j] - mean;
+            ss = __builtin_fmaf(d, d, ss);
         }
+    }
+    const float var = wave_sum(ss) * a.inv_hidden;
+    const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
+
+    const rsrc_t ry = make_rsrc(static_cast<char*>(a.y) + row * a.y_rs,
+                                (uint32_t)a.hidden * sizeof(TY));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        if (!valid[i]) continue;
+        const uint32_t c = i * 64 + lane;
+        Vec<TX, VEC> shv, scv;
+        ms.get(0, c, shv);
+        ms.get(1, c, scv);
+        float sh[VEC], sc[VEC], o[VEC];
+        shv.to_float(sh);
+        scv.to_float(sc);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            o[j] = __builtin_fmaf((v[i][j] - mean) * rstd, 1.0f + sc[j], sh[j]);
+        Vec<TY, VEC> ov;
+        ov.from_float(o);
+        ov.template store_buf<kStoreStream>(ry, c * (VEC * sizeof(TY)));
     }
 }
 
-
 template <typename TX, typename TY, typename TH, int VEC, bool FUSED, int NV>
-hipError_t launch_nv(const AdalnArgs& a, hipStream_t st) {
-    int64_t blocks = (a.rows + kWaves * kRowsPerWave - 1) / (kWaves * kRowsPerWave);
-    if (blocks > 0x7fffffff) blocks = 0x7fffffff;
-    hipLaunchKernelGGL((adaln_kernel<TX, TY, TH, VEC, NV, FUSED>), dim3((unsigned)blocks),
-                       dim3(kWaves * 64), 0, st, a);
+hipError_t launch_nv(const AdalnArgs& a, bool single_group, hipStream_t st) {
+    const int64_t blocks = (a.rows + kWaves - 1) / kWaves;
+    const size_t lds = (size_t)(FUSED ? 3 : 2) * a.nvec * Vec<TX, VEC>::kQuads * 16;
+    // stage in LDS when there is one group and the staged vectors leave room for
+    // several workgroups per CU
+    if (single_group && lds <= 48 * 1024)
+        hipLaunchKernelGGL((adaln_kernel<TX, TY, TH, VEC, NV, FUSED, true>), dim3((unsigned)blocks),
+                           dim3(kWaves * 64), lds, st, a);
+    else
+        hipLaunchKernelGGL((adaln_kernel<TX, TY, TH, VEC, NV, FUSED, false>),
+                           dim3((unsigned)blocks), dim3(kWaves * 64), 0, st, a);
     return hipGetLastError();
 }
 
 template <typename TX, typename TY, typename TH, int VEC, bool FUSED>
-h3f_status_t dispatch(const AdalnArgs& a, int max_nv, hipStream_t st) {
+h3f_status_t dispatch(const AdalnArgs& a, int max_nv, bool single_group, hipStream_t st) {
     const int need = (a.nvec + 63) / 64;
     hipError_t e = hipErrorInvalidValue;
 #define H3F_NV_CASE(N)                                                   \
-    else if (need <= N && N <= max_nv) e = launch_nv<TX, TY, TH, VEC, FUSED, N>(a, st);
+    else if (need <= N && N <= max_nv) e = launch_nv<TX, TY, TH, VEC, FUSED, N>(a, single_group, st);
     if (false) {
     }
     H3F_NV_CASE(1) H3F_NV_CASE(2) H3F_NV_CASE(3) H3F_NV_CASE(4) H3F_NV_CASE(5) H3F_NV_CASE(6)
@@ -217,24 +256,26 @@ extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t
 
     AdalnArgs a{};
     a.y = y;
-    a.y_rs = rows > 1 ? y_row_stride : hidden;
+    a.y_rs = (rows > 1 ? y_row_stride : hidden) * ey;
     a.x = const_cast<void*>(x);
-    a.x_rs = rows > 1 ? x_row_stride : hidden;
+    a.x_rs = (rows > 1 ? x_row_stride : hidden) * ex;
     a.shift = shift;
     a.scale = scale;
-    a.mod_gs = groups > 1 ? mod_group_stride : 0;
+    a.mod_gs = (groups > 1 ? mod_group_stride : 0) * ex;
     a.div_group = make_fastdiv((uint32_t)(rows_per_group > rows ? rows : rows_per_group));
     a.rows = rows;
     a.nvec = (int32_t)(hidden / V);
+    a.hidden = (int32_t)hidden;
     a.inv_hidden = 1.0f / (float)hidden;
     a.eps = eps;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int mnv = max_nv_for(x_dtype, V);
+    const bool one = groups == 1;
     if (x_dtype == H3F_F32 && y_dtype == H3F_F32)
-        return dispatch<float, float, float, 4, false>(a, mnv, st);
+        return dispatch<float, float, float, 4, false>(a, mnv, one, st);
     if (x_dtype == H3F_BF16)
-        return dispatch<__bf16, __bf16, __bf16, 8, false>(a, mnv, st);
-    return dispatch<float, __bf16, float, 8, false>(a, mnv, st);
+        return dispatch<__bf16, __bf16, __bf16, 8, false>(a, mnv, one, st);
+    return dispatch<float, __bf16, float, 8, false>(a, mnv, one, st);
 }
 
 extern "C" h3f_status_t h3f_gated_residual_adaln(
@@ -278,26 +319,28 @@ extern "C" h3f_status_t h3f_gated_residual_adaln(
 
     AdalnArgs a{};
     a.y = y;
-    a.y_rs = rows > 1 ? y_row_stride : hidden;
+    a.y_rs = (rows > 1 ? y_row_stride : hidden) * ey;
     a.x = x;
-    a.x_rs = rows > 1 ? x_row_stride : hidden;
+    a.x_rs = (rows > 1 ? x_row_stride : hidden) * ex;
     a.h = h;
-    a.h_rs = rows > 1 ? h_row_stride : hidden;
+    a.h_rs = (rows > 1 ? h_row_stride : hidden) * eh;
     a.gate = gate;
     a.shift = shift;
     a.scale = scale;
-    a.mod_gs = groups > 1 ? mod_group_stride : 0;
+    a.mod_gs = (groups > 1 ? mod_group_stride : 0) * ex;
     a.div_group = make_fastdiv((uint32_t)(rows_per_group > rows ? rows : rows_per_group));
     a.rows = rows;
     a.nvec = (int32_t)(hidden / V);
+    a.hidden = (int32_t)hidden;
     a.inv_hidden = 1.0f / (float)hidden;
     a.eps = eps;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int mnv = max_nv_for(x_dtype, V);
-    if (x_dtype == H3F_BF16) return dispatch<__bf16, __bf16, __bf16, 8, true>(a, mnv, st);
+    const bool one = groups == 1;
+    if (x_dtype == H3F_BF16) return dispatch<__bf16, __bf16, __bf16, 8, true>(a, mnv, one, st);
     if (h_dtype == H3F_F32 && y_dtype == H3F_F32)
-        return dispatch<float, float, float, 4, true>(a, mnv, st);
-    if (h_dtype == H3F_F32) return dispatch<float, __bf16, float, 8, true>(a, mnv, st);
-    if (y_dtype == H3F_F32) return dispatch<float, float, __bf16, 8, true>(a, mnv, st);
-    return dispatch<float, __bf16, __bf16, 8, true>(a, mnv, st);
+        return dispatch<float, float, float, 4, true>(a, mnv, one, st);
+    if (h_dtype == H3F_F32) return dispatch<float, __bf16, float, 8, true>(a, mnv, one, st);
+    if (y_dtype == H3F_F32) return dispatch<float, float, __bf16, 8, true>(a, mnv, one, st);
+    return dispatch<float, __bf16, __bf16, 8, true>(a, mnv, one, st);
 }

@@ -18,37 +18,65 @@
 namespace h3f {
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kUnroll = 4;
+#ifndef H3F_EW_BLOCK
+#define H3F_EW_BLOCK 64
+#endif
+#ifndef H3F_EW_UNROLL
+#define H3F_EW_UNROLL 1
+#endif
+constexpr int kBlock = H3F_EW_BLOCK;
+constexpr int kUnroll = H3F_EW_UNROLL;
+constexpr int kTile = kBlock * kUnroll;
 // Largest number of chunks one launch indexes with 32-bit arithmetic.
-constexpr int64_t kMaxChunksPerLaunch = (int64_t(1) << 31) - kBlock * kUnroll;
+constexpr int64_t kMaxChunksPerLaunch = (int64_t(1) << 31) - kTile;
+
+// A workgroup's tile of kTile consecutive chunks spans rows [row0, row0 + k); each
+// tensor is addressed through a buffer resource based at its row row0, so all
+// in-tile offsets are 32-bit and chunks past the tensor's end are dropped.
+struct Stream {
+    const char* base;  // element (0, 0) of the launch
+    int64_t stride;    // bytes between rows
+    int64_t rows;      // rows of the launch (or groups, for a modulation tensor)
+    int32_t row_bytes; // bytes of one row that are touched
+};
+
+__device__ __forceinline__ rsrc_t tile_rsrc(const Stream& s, uint32_t r0) {
+    return make_rsrc(s.base + (int64_t)r0 * s.stride,
+                     span_bytes(s.rows - (int64_t)r0, s.stride, s.row_bytes));
+}
 
 // ---------------------------------------------------------------------------
 // Gated residual: x[r, :] += gate[g(r), :] * h[r, :]   (fp32 arithmetic)
 // ---------------------------------------------------------------------------
 template <typename TX, typename TH, int VEC>
 __global__ void __launch_bounds__(kBlock)
-gated_residual_kernel(TX* __restrict__ x, int64_t x_rs, const TH* __restrict__ h, int64_t h_rs,
-                      const TX* __restrict__ gate, int64_t gate_gs, FastDiv div_cols,
-                      FastDiv div_group, uint32_t row_base, uint32_t n_chunks) {
-    const uint32_t base = blockIdx.x * (uint32_t)(kBlock * kUnroll) + threadIdx.x;
+gated_residual_kernel(Stream xs, Stream hs, Stream gs, FastDiv div_cols, FastDiv div_group,
+                      uint32_t row_base, uint32_t n_chunks) {
+    const uint32_t tile0 = blockIdx.x * (uint32_t)kTile;
+    const uint32_t row0 = fdiv(tile0, div_cols);
+    const uint32_t g0 = fdiv(row_base + row0, div_group);
+    const rsrc_t rx = tile_rsrc(xs, row0);
+    const rsrc_t rh = tile_rsrc(hs, row0);
+    const rsrc_t rg = tile_rsrc(gs, g0);
     Vec<TX, VEC> xv[kUnroll];
     Vec<TH, VEC> hv[kUnroll];
     Vec<TX, VEC> gv[kUnroll];
-    int64_t xoff[kUnroll];
+    uint32_t xoff[kUnroll];
     bool ok[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t idx = base + u * kBlock;
+        const uint32_t idx = tile0 + u * kBlock + threadIdx.x;
         ok[u] = idx < n_chunks;
         const uint32_t row = fdiv(idx, div_cols);
-        const uint32_t col = (idx - row * div_cols.d) * VEC;
+        const uint32_t col = idx - row * div_cols.d;
         const uint32_t grp = fdiv(row_base + row, div_group);
-        xoff[u] = (int64_t)row * x_rs + col;
+        xoff[u] = (row - row0) * (uint32_t)xs.stride + col * (uint32_t)(VEC * sizeof(TX));
         if (ok[u]) {
-            xv[u].template load<true>(x + xoff[u]);
-            hv[u].template load<true>(h + (int64_t)row * h_rs + col);
-            gv[u].template load<false>(gate + (int64_t)grp * gate_gs + col);
+            xv[u].template load_buf<kLoadStream>(rx, xoff[u]);
+            hv[u].template load_buf<kLoadStream>(
+                rh, (row - row0) * (uint32_t)hs.stride + col * (uint32_t)(VEC * sizeof(TH)));
+            gv[u].template load_buf<kLoadReuse>(
+                rg, (grp - g0) * (uint32_t)gs.stride + col * (uint32_t)(VEC * sizeof(TX)));
         }
     }
 #pragma unroll
@@ -61,7 +89,7 @@ gated_residual_kernel(TX* __restrict__ x, int64_t x_rs, const TH* __restrict__ h
 #pragma unroll
         for (int i = 0; i < VEC; ++i) xf[i] = __builtin_fmaf(gf[i], hf[i], xf[i]);
         xv[u].from_float(xf);
-        xv[u].template store<true>(x + xoff[u]);
+        xv[u].template store_buf<kStoreStream>(rx, xoff[u]);
     }
 }
 
@@ -76,22 +104,26 @@ __device__ __forceinline__ float silu_f(float a) {
 
 template <typename T, int VEC>
 __global__ void __launch_bounds__(kBlock)
-swiglu_kernel(T* __restrict__ out, int64_t o_rs, const T* __restrict__ a, int64_t a_rs,
-              const T* __restrict__ b, int64_t b_rs, FastDiv div_cols, uint32_t n_chunks) {
-    const uint32_t base = blockIdx.x * (uint32_t)(kBlock * kUnroll) + threadIdx.x;
+swiglu_kernel(Stream os, Stream as, Stream bs, FastDiv div_cols, uint32_t n_chunks) {
+    const uint32_t tile0 = blockIdx.x * (uint32_t)kTile;
+    const uint32_t row0 = fdiv(tile0, div_cols);
+    const rsrc_t ro = tile_rsrc(os, row0);
+    const rsrc_t ra = tile_rsrc(as, row0);
+    const rsrc_t rb = tile_rsrc(bs, row0);
     Vec<T, VEC> av[kUnroll], bv[kUnroll];
-    int64_t ooff[kUnroll];
+    uint32_t ooff[kUnroll];
     bool ok[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t idx = base + u * kBlock;
+        const uint32_t idx = tile0 + u * kBlock + threadIdx.x;
         ok[u] = idx < n_chunks;
         const uint32_t row = fdiv(idx, div_cols);
-        const uint32_t col = (idx - row * div_cols.d) * VEC;
-        ooff[u] = (int64_t)row * o_rs + col;
+        const uint32_t rr = row - row0;
+        const uint32_t cb = (idx - row * div_cols.d) * (uint32_t)(VEC * sizeof(T));
+        ooff[u] = rr * (uint32_t)os.stride + cb;
         if (ok[u]) {
-            av[u].template load<true>(a + (int64_t)row * a_rs + col);
-            bv[u].template load<true>(b + (int64_t)row * b_rs + col);
+            av[u].template load_buf<kLoadStream>(ra, rr * (uint32_t)as.stride + cb);
+            bv[u].template load_buf<kLoadStream>(rb, rr * (uint32_t)bs.stride + cb);
         }
     }
 #pragma unroll
@@ -104,31 +136,31 @@ swiglu_kernel(T* __restrict__ out, int64_t o_rs, const T* __restrict__ a, int64_
         for (int i = 0; i < VEC; ++i) of[i] = silu_f(af[i]) * bf[i];
         Vec<T, VEC> ov;
         ov.from_float(of);
-        ov.template store<true>(out + ooff[u]);
+        ov.template store_buf<kStoreStream>(ro, ooff[u]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Streaming copy (measurement helper).
+// Streaming copy (measurement helper): the same access pattern and cache
+// policy as the operators, one 16-byte chunk per thread and unroll step.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kBlock)
-stream_copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, uint64_t n_quads) {
-    const uint64_t base = (uint64_t)blockIdx.x * (kBlock * kUnroll) + threadIdx.x;
+stream_copy_kernel(char* __restrict__ dst, const char* __restrict__ src, uint64_t bytes) {
+    const uint64_t tile_bytes = (uint64_t)kTile * 16;
+    const uint64_t t0 = (uint64_t)blockIdx.x * tile_bytes;
+    const uint64_t left = bytes - t0;
+    const uint32_t nb = left < tile_bytes ? (uint32_t)left : (uint32_t)tile_bytes;
+    const rsrc_t rs = make_rsrc(src + t0, nb);
+    const rsrc_t rd = make_rsrc(dst + t0, nb);
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t i = base + (uint64_t)u * kBlock;
-        if (i < n_quads) v[u] = ld16_nt(src + i);
-    }
+    for (int u = 0; u < kUnroll; ++u) v[u] = buf_ld<kLoadStream>(rs, 16u * (u * kBlock + threadIdx.x));
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t i = base + (uint64_t)u * kBlock;
-        if (i < n_quads) st16_nt(dst + i, v[u]);
-    }
+    for (int u = 0; u < kUnroll; ++u) buf_st<kStoreStream>(rd, 16u * (u * kBlock + threadIdx.x), v[u]);
 }
 
 inline unsigned blocks_for(int64_t chunks) {
-    return (unsigned)((chunks + kBlock * kUnroll - 1) / (kBlock * kUnroll));
+    return (unsigned)((chunks + kTile - 1) / kTile);
 }
 
 // Rows per launch so that rows * chunks_per_row stays inside 32-bit indexing.
@@ -137,20 +169,43 @@ inline int64_t rows_per_launch(int64_t chunks_per_row) {
     return r < 1 ? 1 : r;
 }
 
+// In-tile byte offsets are 32-bit: a tile covers at most this many rows.
+inline bool tile_fits(int64_t chunks_per_row, int64_t stride_bytes, int64_t row_bytes) {
+    const int64_t tile_rows = kTile / chunks_per_row + 2;
+    return tile_rows * stride_bytes + row_bytes < 0xFFFFFFF0ll;
+}
+
+inline Stream stream_of(const void* base, int64_t stride_elems, int64_t rows, int64_t cols,
+                        int esize) {
+    Stream s;
+    s.base = static_cast<const char*>(base);
+    s.stride = stride_elems * esize;
+    s.rows = rows;
+    s.row_bytes = (int32_t)(cols * esize);
+    return s;
+}
+
 template <typename TX, typename TH, int VEC>
 h3f_status_t launch_gated(void* x, int64_t x_rs, const void* h, int64_t h_rs, const void* gate,
                           int64_t gate_gs, int64_t rows_per_group, int64_t rows, int64_t hidden,
                           hipStream_t st) {
     const int64_t cpr = hidden / VEC;
+    if (!tile_fits(cpr, x_rs * (int64_t)sizeof(TX), hidden * (int64_t)sizeof(TX)) ||
+        !tile_fits(cpr, h_rs * (int64_t)sizeof(TH), hidden * (int64_t)sizeof(TH)) ||
+        !tile_fits(cpr, gate_gs * (int64_t)sizeof(TX), hidden * (int64_t)sizeof(TX)))
+        return H3F_ERR_UNSUPPORTED;
     const int64_t step = rows_per_launch(cpr);
     const int64_t rpg = rows_per_group > rows ? rows : rows_per_group;
+    const int64_t groups = (rows + rpg - 1) / rpg;
+    const Stream gs = stream_of(gate, gate_gs, groups, hidden, sizeof(TX));
     for (int64_t r0 = 0; r0 < rows; r0 += step) {
         const int64_t nr = rows - r0 < step ? rows - r0 : step;
         const uint32_t n = (uint32_t)(nr * cpr);
+        const Stream xs = stream_of(static_cast<TX*>(x) + r0 * x_rs, x_rs, nr, hidden, sizeof(TX));
+        const Stream hs =
+            stream_of(static_cast<const TH*>(h) + r0 * h_rs, h_rs, nr, hidden, sizeof(TH));
         hipLaunchKernelGGL((gated_residual_kernel<TX, TH, VEC>), dim3(blocks_for(n)), dim3(kBlock),
-                           0, st, static_cast<TX*>(x) + r0 * x_rs, x_rs,
-                           static_cast<const TH*>(h) + r0 * h_rs, h_rs,
-                           static_cast<const TX*>(gate), gate_gs, make_fastdiv((uint32_t)cpr),
+                           0, st, xs, hs, gs, make_fastdiv((uint32_t)cpr),
                            make_fastdiv((uint32_t)rpg), (uint32_t)r0, n);
     }
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
@@ -160,15 +215,19 @@ template <typename T, int VEC>
 h3f_status_t launch_swiglu(void* out, int64_t o_rs, const void* a, int64_t a_rs, const void* b,
                            int64_t b_rs, int64_t rows, int64_t inner, hipStream_t st) {
     const int64_t cpr = inner / VEC;
+    const int64_t e = sizeof(T);
+    if (!tile_fits(cpr, o_rs * e, inner * e) || !tile_fits(cpr, a_rs * e, inner * e) ||
+        !tile_fits(cpr, b_rs * e, inner * e))
+        return H3F_ERR_UNSUPPORTED;
     const int64_t step = rows_per_launch(cpr);
     for (int64_t r0 = 0; r0 < rows; r0 += step) {
         const int64_t nr = rows - r0 < step ? rows - r0 : step;
         const uint32_t n = (uint32_t)(nr * cpr);
-        hipLaunchKernelGGL((swiglu_kernel<T, VEC>), dim3(blocks_for(n)), dim3(kBlock), 0, st,
-                           static_cast<T*>(out) + r0 * o_rs, o_rs,
-                           static_cast<const T*>(a) + r0 * a_rs, a_rs,
-                           static_cast<const T*>(b) + r0 * b_rs, b_rs,
-                           make_fastdiv((uint32_t)cpr), n);
+        const Stream os = stream_of(static_cast<T*>(out) + r0 * o_rs, o_rs, nr, inner, e);
+        const Stream as = stream_of(static_cast<const T*>(a) + r0 * a_rs, a_rs, nr, inner, e);
+        const Stream bs = stream_of(static_cast<const T*>(b) + r0 * b_rs, b_rs, nr, inner, e);
+        hipLaunchKernelGGL((swiglu_kernel<T, VEC>), dim3(blocks_for(n)), dim3(kBlock), 0, st, os,
+                           as, bs, make_fastdiv((uint32_t)cpr), n);
     }
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }
@@ -254,10 +313,10 @@ extern "C" h3f_status_t h3f_stream_copy(void* dst, const void* src, int64_t byte
     const Region rs = region2d(src, 1, 0, bytes, 1);
     if (!disjoint(rd, rs)) return H3F_ERR_ALIASING;
     const uint64_t n = (uint64_t)bytes / 16;
-    const uint64_t blocks = (n + kBlock * kUnroll - 1) / (kBlock * kUnroll);
+    const uint64_t blocks = (n + kTile - 1) / kTile;
     if (blocks > 0xffffffffull) return H3F_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
-                       static_cast<hipStream_t>(stream), static_cast<u32x4*>(dst),
-                       static_cast<const u32x4*>(src), n);
+                       static_cast<hipStream_t>(stream), static_cast<char*>(dst),
+                       static_cast<const char*>(src), (uint64_t)bytes);
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }

@@ -1,18 +1,23 @@
 // k_qk_rope.hip -- per-head QK RMSNorm fused with 3D RoPE, and the token
 // position helper.
 //
-// Design (gfx950): one 64-wide wavefront owns one token row at a time.  A head
-// of head_dim elements is LPH = head_dim / VEC lanes of one 16-byte chunk each
-// (bf16 head_dim 128: 16 lanes, i.e. one DPP row), so a wavefront instruction
-// covers 64 / LPH head-rows and the token's 2 * heads head-rows of q and k take
-// ceil(2 * heads * LPH / 64) loads, issued CH at a time before any is consumed.
+// Design (gfx950): a head of head_dim elements is LPH = head_dim / VEC lanes of
+// one 16-byte chunk each (bf16 head_dim 128: 16 lanes, one DPP row), so one
+// wavefront load covers GPW = 64 / LPH head-rows.  The token's q heads take
+// nl = ceil(heads / GPW) such loads and its k heads another nl; each of these
+// 2 * nl "slots" of each token is one independent 64-thread workgroup that does
+// exactly one 16-byte load and one 16-byte store per lane.  Measured on MI355X,
+// this finest work granularity streams best (many short wavefronts, about one
+// KiB in flight each); a wavefront that holds a whole token row is ~10% slower.
 // The RMS of a head is a DPP reduction inside its LPH lanes (no LDS, no
-// barrier).  The lane owns whole rotation pairs (interleaved layout) or fetches
-// its partner chunk with a lane shuffle (half-split layout).  The token's
-// position is wave-uniform; cos / sin of the lane's pairs are generated in
-// registers once per token and reused for all 2 * heads head-rows.
+// barrier).  The token's position is wave-uniform scalar arithmetic.  cos / sin
+// are generated in registers: with the interleaved layout and at most 64
+// rotation pairs, lane L computes pair L once and the lanes of each head fetch
+// their pairs with lane shuffles; otherwise each lane computes its own pairs.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 
 #include "h3f_device.hpp"
 #include "h3f_validate.hpp"
@@ -20,31 +25,32 @@
 namespace h3f {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 2;
 constexpr int kMaxPairs = 256;
 
+// Token grid: row r (of the whole call) is token p = (offset + r) mod period;
+// offset is reduced modulo period on the host and offset + rows < 2^31.
 struct GridArgs {
-    int32_t T, H, W, n_audio;
-    int64_t n_video;  // T * H * W
-    int64_t period;   // n_video + n_audio
-    int64_t token_offset;
-    const int32_t* positions;
+    uint32_t n_video, period, offset, W, HW;
+    FastDiv div_period, div_hw, div_w;
+    const int32_t* positions;  // optional [rows, 3]
 };
 
+// Row / head strides in bytes.
 struct QKArgs {
-    void* q_out;
+    char* q_out;
     int64_t qo_rs, qo_hs;
-    void* k_out;
+    char* k_out;
     int64_t ko_rs, ko_hs;
-    const void* q;
+    const char* q;
     int64_t q_rs, q_hs;
-    const void* k;
+    const char* k;
     int64_t k_rs, k_hs;
-    const void* qw;
-    const void* kw;
-    int64_t rows;
-    int32_t heads;
+    uint32_t qo_span, ko_span, q_span, k_span;  // bytes of one row's heads
+    const char* qw;
+    const char* kw;
+    int64_t row0;      // first row of this launch
+    FastDiv div_slots; // 2 * nl slots per token
+    int32_t nl;        // loads per tensor per token
     int32_t head_dim;
     float inv_head_dim;
     float eps;
@@ -62,13 +68,15 @@ __device__ __forceinline__ void token_position(const GridArgs& g, int64_t row, i
         w = g.positions[3 * row + 2];
         return;
     }
-    const int64_t p = (g.token_offset + row) % g.period;
+    uint32_t p = g.offset + (uint32_t)row;
+    p -= fdiv(p, g.div_period) * g.period;
     if (p < g.n_video) {
-        const int64_t hw = (int64_t)g.H * g.W;
-        t = (int32_t)(p / hw);
-        const int64_t rem = p - (int64_t)t * hw;
-        h = (int32_t)(rem / g.W);
-        w = (int32_t)(rem - (int64_t)h * g.W);
+        const uint32_t tt = fdiv(p, g.div_hw);
+        const uint32_t rem = p - tt * g.HW;
+        const uint32_t hh = fdiv(rem, g.div_w);
+        t = (int32_t)tt;
+        h = (int32_t)hh;
+        w = (int32_t)(rem - hh * g.W);
     } else {
         t = (int32_t)(p - g.n_video);
         h = 0;
@@ -76,116 +84,104 @@ __device__ __forceinline__ void token_position(const GridArgs& g, int64_t row, i
     }
 }
 
-template <typename T, int VEC, int LPH, int CH, bool HALF>
-__global__ void __launch_bounds__(kWaves * 64) qk_rmsnorm_rope3d_kernel(QKArgs a) {
-    constexpr int GPW = 64 / LPH;                 // head-rows per wavefront load
-    constexpr int NA = HALF ? VEC : VEC / 2;      // angles per lane
-    const int lane = threadIdx.x & 63;
-    const int gsub = lane / LPH;                  // head-row slot of this lane
-    const int e0 = (lane % LPH) * VEC;            // first element of the lane in its head
-    const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+template <typename T, int VEC, int LPH, bool HALF>
+__global__ void __launch_bounds__(64) qk_rmsnorm_rope3d_kernel(QKArgs a) {
+    constexpr int GPW = 64 / LPH;             // head-rows per wavefront load
+    constexpr int NA = HALF ? VEC : VEC / 2;  // rotation pairs touched by a lane
+    constexpr bool kShared = !HALF && LPH * VEC / 2 <= 64;
+    const int lane = threadIdx.x;
+    const int gsub = lane / LPH;        // head-row slot of this lane
+    const int e0 = (lane % LPH) * VEC;  // first element of the lane in its head
 
-    // Axis of the lane's elements, rotation pair ids and partner lane.
-    const int axis = e0 < a.c1 ? 0 : (e0 < a.c2 ? 1 : 2);
-    const int cstart = axis == 0 ? 0 : (axis == 1 ? a.c1 : a.c2);
-    const int cend = axis == 0 ? a.c1 : (axis == 1 ? a.c2 : a.head_dim);
-    const int chalf = (cend - cstart) / 2;
-    const bool first_half = (e0 - cstart) < chalf;
-    float freq[NA];
-#pragma unroll
-    for (int m = 0; m < NA; ++m) {
-        int pair;
-        if (HALF)
-            pair = cstart / 2 + ((e0 - cstart + m) % chalf);
-        else
-            pair = e0 / 2 + m;
-        freq[m] = a.inv_freq[pair];
-    }
-    const int partner = HALF ? (first_half ? lane + chalf / VEC : lane - chalf / VEC) : lane;
+    // Which token and which slot: wave-uniform.
+    const uint32_t bid = blockIdx.x;
+    const uint32_t rr = fdiv(bid, a.div_slots);
+    const uint32_t slot = bid - rr * a.div_slots.d;
+    const int64_t row = a.row0 + rr;
+    const bool isk = slot >= (uint32_t)a.nl;
+    const uint32_t hd = (isk ? slot - a.nl : slot) * GPW + gsub;
 
-    // Norm weights of the lane's elements, for q and for k.
-    float wq[VEC], wk[VEC];
+    // One 16-byte chunk per lane; a head slot past the last head lies outside the
+    // row's resource (offset >= heads * head_stride >= span): reads 0, not stored.
+    const rsrc_t rin = isk ? make_rsrc(a.k + row * a.k_rs, a.k_span)
+                           : make_rsrc(a.q + row * a.q_rs, a.q_span);
+    const uint32_t e0b = (uint32_t)e0 * sizeof(T);
+    Vec<T, VEC> buf;
+    buf.template load_buf<kLoadStream>(rin, hd * (uint32_t)(isk ? a.k_hs : a.q_hs) + e0b);
+
+    float w[VEC];
     {
         Vec<T, VEC> t;
-        t.template load<false>(static_cast<const T*>(a.qw) + e0);
-        t.to_float(wq);
-        t.template load<false>(static_cast<const T*>(a.kw) + e0);
-        t.to_float(wk);
+        t.template load<false>(reinterpret_cast<const T*>(isk ? a.kw : a.qw) + e0);
+        t.to_float(w);
     }
 
-    const int head_rows = 2 * a.heads;
-    const int n_loads = (head_rows + GPW - 1) / GPW;
-
-    for (int64_t row = wave; row < a.rows; row += nwaves) {
-        int32_t pt, ph, pw;
-        token_position(a.grid, row, pt, ph, pw);
-        const float pf = (float)(axis == 0 ? pt : (axis == 1 ? ph : pw));
-        float cs[NA], sn[NA];
+    // Angles of the lane's rotation pairs at this token.
+    int32_t pt, ph, pw;
+    token_position(a.grid, row, pt, ph, pw);
+    float cs[NA], sn[NA];
+    if constexpr (kShared) {
+        // lane L holds pair L (pair p covers elements 2p, 2p + 1)
+        const int e = 2 * lane;
+        const int ax = e < a.c1 ? 0 : (e < a.c2 ? 1 : 2);
+        const float pf = (float)(ax == 0 ? pt : (ax == 1 ? ph : pw));
+        float s1 = 0.f, c1 = 1.f;
+        if (lane < LPH * VEC / 2) sincosf(pf * a.inv_freq[lane], &s1, &c1);
 #pragma unroll
         for (int m = 0; m < NA; ++m) {
-            const float phi = pf * freq[m];
-            sincosf(phi, &sn[m], &cs[m]);
+            cs[m] = __shfl(c1, e0 / 2 + m, 64);
+            sn[m] = __shfl(s1, e0 / 2 + m, 64);
         }
-
-        for (int l0 = 0; l0 < n_loads; l0 += CH) {
-            Vec<T, VEC> buf[CH];
-            const T* src[CH];
-            T* dst[CH];
-            bool ok[CH], isk[CH];
+    } else {
+        const int ax = e0 < a.c1 ? 0 : (e0 < a.c2 ? 1 : 2);
+        const int cstart = ax == 0 ? 0 : (ax == 1 ? a.c1 : a.c2);
+        const int cend = ax == 0 ? a.c1 : (ax == 1 ? a.c2 : a.head_dim);
+        const int chalf = (cend - cstart) / 2;
+        const float pf = (float)(ax == 0 ? pt : (ax == 1 ? ph : pw));
 #pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                const int hr = (l0 + j) * GPW + gsub;
-                ok[j] = hr < head_rows;
-                isk[j] = hr >= a.heads;
-                const int hd = isk[j] ? hr - a.heads : hr;
-                if (isk[j]) {
-                    src[j] = static_cast<const T*>(a.k) + row * a.k_rs + (int64_t)hd * a.k_hs + e0;
-                    dst[j] = static_cast<T*>(a.k_out) + row * a.ko_rs + (int64_t)hd * a.ko_hs + e0;
-                } else {
-                    src[j] = static_cast<const T*>(a.q) + row * a.q_rs + (int64_t)hd * a.q_hs + e0;
-                    dst[j] = static_cast<T*>(a.q_out) + row * a.qo_rs + (int64_t)hd * a.qo_hs + e0;
-                }
-                if (ok[j])
-                    buf[j].template load<true>(src[j]);
-                else
-                    buf[j].zero();
-            }
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                float v[VEC];
-                buf[j].to_float(v);
-                float ss = 0.f;
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
-                ss = group_sum<LPH>(ss);
-                const float rstd = __builtin_amdgcn_rsqf(ss * a.inv_head_dim + a.eps);
-                float u[VEC];
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) u[i] = v[i] * rstd * (isk[j] ? wk[i] : wq[i]);
-                float o[VEC];
-                if constexpr (!HALF) {
-#pragma unroll
-                    for (int m = 0; m < VEC / 2; ++m) {
-                        const float u0 = u[2 * m], u1 = u[2 * m + 1];
-                        o[2 * m] = u0 * cs[m] - u1 * sn[m];
-                        o[2 * m + 1] = u0 * sn[m] + u1 * cs[m];
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) {
-                        const float pv = __shfl(u[i], partner, 64);
-                        o[i] = first_half ? u[i] * cs[i] - pv * sn[i] : pv * sn[i] + u[i] * cs[i];
-                    }
-                }
-                if (ok[j]) {
-                    Vec<T, VEC> ov;
-                    ov.from_float(o);
-                    ov.template store<true>(dst[j]);
-                }
-            }
+        for (int m = 0; m < NA; ++m) {
+            const int pair = HALF ? cstart / 2 + ((e0 - cstart + m) % chalf) : e0 / 2 + m;
+            sincosf(pf * a.inv_freq[pair], &sn[m], &cs[m]);
         }
     }
+
+    float v[VEC];
+    buf.to_float(v);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+    ss = group_sum<LPH>(ss);
+    const float rstd = __builtin_amdgcn_rsqf(ss * a.inv_head_dim + a.eps);
+    float u[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) u[i] = v[i] * rstd * w[i];
+    float o[VEC];
+    if constexpr (!HALF) {
+#pragma unroll
+        for (int m = 0; m < VEC / 2; ++m) {
+            const float u0 = u[2 * m], u1 = u[2 * m + 1];
+            o[2 * m] = u0 * cs[m] - u1 * sn[m];
+            o[2 * m + 1] = u0 * sn[m] + u1 * cs[m];
+        }
+    } else {
+        // pairs (j, j + d_c/2): the partner chunk sits chalf / VEC lanes away
+        const int ax = e0 < a.c1 ? 0 : (e0 < a.c2 ? 1 : 2);
+        const int cstart = ax == 0 ? 0 : (ax == 1 ? a.c1 : a.c2);
+        const int cend = ax == 0 ? a.c1 : (ax == 1 ? a.c2 : a.head_dim);
+        const int chalf = (cend - cstart) / 2;
+        const bool first = (e0 - cstart) < chalf;
+        const int partner = first ? lane + chalf / VEC : lane - chalf / VEC;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const float pv = __shfl(u[i], partner, 64);
+            o[i] = first ? u[i] * cs[i] - pv * sn[i] : pv * sn[i] + u[i] * cs[i];
+        }
+    }
+    Vec<T, VEC> ov;
+    ov.from_float(o);
+    const rsrc_t rout = isk ? make_rsrc(a.k_out + row * a.ko_rs, a.ko_span)
+                            : make_rsrc(a.q_out + row * a.qo_rs, a.qo_span);
+    ov.template store_buf<kStoreStream>(rout, hd * (uint32_t)(isk ? a.ko_hs : a.qo_hs) + e0b);
 }
 
 __global__ void __launch_bounds__(256) positions_kernel(int32_t* __restrict__ pos, int64_t rows,
@@ -199,44 +195,56 @@ __global__ void __launch_bounds__(256) positions_kernel(int32_t* __restrict__ po
     pos[3 * r + 2] = w;
 }
 
-constexpr int kCH = 10;
-
 template <typename T, int VEC, int LPH, bool HALF>
-hipError_t launch_lph(const QKArgs& a, hipStream_t st) {
-    int64_t blocks = (a.rows + kWaves * kRowsPerWave - 1) / (kWaves * kRowsPerWave);
-    if (blocks > 0x7fffffff) blocks = 0x7fffffff;
-    hipLaunchKernelGGL((qk_rmsnorm_rope3d_kernel<T, VEC, LPH, kCH, HALF>), dim3((unsigned)blocks),
-                       dim3(kWaves * 64), 0, st, a);
+hipError_t launch_lph(QKArgs a, int64_t rows, hipStream_t st) {
+    const int64_t slots = a.div_slots.d;
+    const int64_t step = 0x7fffffffll / slots;
+    for (int64_t r0 = 0; r0 < rows; r0 += step) {
+        const int64_t nr = rows - r0 < step ? rows - r0 : step;
+        a.row0 = r0;
+        hipLaunchKernelGGL((qk_rmsnorm_rope3d_kernel<T, VEC, LPH, HALF>),
+                           dim3((unsigned)(nr * slots)), dim3(64), 0, st, a);
+    }
     return hipGetLastError();
 }
 
 template <typename T, int VEC, bool HALF>
-hipError_t dispatch_lph(const QKArgs& a, int lph, hipStream_t st) {
+hipError_t dispatch_lph(const QKArgs& a, int lph, int64_t rows, hipStream_t st) {
     switch (lph) {
-        case 2: return launch_lph<T, VEC, 2, HALF>(a, st);
-        case 4: return launch_lph<T, VEC, 4, HALF>(a, st);
-        case 8: return launch_lph<T, VEC, 8, HALF>(a, st);
-        case 16: return launch_lph<T, VEC, 16, HALF>(a, st);
-        case 32: return launch_lph<T, VEC, 32, HALF>(a, st);
-        case 64: return launch_lph<T, VEC, 64, HALF>(a, st);
+        case 2: return launch_lph<T, VEC, 2, HALF>(a, rows, st);
+        case 4: return launch_lph<T, VEC, 4, HALF>(a, rows, st);
+        case 8: return launch_lph<T, VEC, 8, HALF>(a, rows, st);
+        case 16: return launch_lph<T, VEC, 16, HALF>(a, rows, st);
+        case 32: return launch_lph<T, VEC, 32, HALF>(a, rows, st);
+        case 64: return launch_lph<T, VEC, 64, HALF>(a, rows, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-h3f_status_t grid_args(const h3f_rope3d_t* r, GridArgs& g) {
+// Grid description for the kernels; rows + reduced offset must stay below 2^31.
+h3f_status_t grid_args(const h3f_rope3d_t* r, int64_t rows, GridArgs& g) {
     g.positions = r->positions;
-    g.T = r->T;
-    g.H = r->H;
-    g.W = r->W;
-    g.n_audio = r->n_audio;
-    g.token_offset = r->token_offset;
-    if (!r->positions) {
-        if (r->T < 1 || r->H < 1 || r->W < 1 || r->n_audio < 0) return H3F_ERR_BAD_SHAPE;
-        if (r->token_offset < 0) return H3F_ERR_BAD_SHAPE;
+    if (r->positions) {
+        g.n_video = g.period = g.offset = g.W = g.HW = 1;
+        g.div_period = g.div_hw = g.div_w = make_fastdiv(1);
+        return H3F_OK;
     }
-    g.n_video = (int64_t)(r->T > 0 ? r->T : 0) * (r->H > 0 ? r->H : 0) * (r->W > 0 ? r->W : 0);
-    g.period = g.n_video + (r->n_audio > 0 ? r->n_audio : 0);
-    if (g.period < 1) g.period = 1;
+    if (r->T < 1 || r->H < 1 || r->W < 1 || r->n_audio < 0) return H3F_ERR_BAD_SHAPE;
+    if (r->token_offset < 0) return H3F_ERR_BAD_SHAPE;
+    const int64_t hw = (int64_t)r->H * r->W;
+    const int64_t nv = hw * r->T;
+    const int64_t period = nv + r->n_audio;
+    if (period > 0x7fffffffll) return H3F_ERR_UNSUPPORTED;
+    const int64_t off = r->token_offset % period;
+    if (off + rows > 0x7fffffffll) return H3F_ERR_UNSUPPORTED;
+    g.n_video = (uint32_t)nv;
+    g.period = (uint32_t)period;
+    g.offset = (uint32_t)off;
+    g.W = (uint32_t)r->W;
+    g.HW = (uint32_t)hw;
+    g.div_period = make_fastdiv(g.period);
+    g.div_hw = make_fastdiv(g.HW);
+    g.div_w = make_fastdiv(g.W);
     return H3F_OK;
 }
 
@@ -254,10 +262,9 @@ extern "C" h3f_status_t h3f_rope3d_positions(int32_t* pos, int64_t rows, const h
     h3f_rope3d_t g = *grid;
     g.positions = nullptr;
     GridArgs ga;
-    h3f_status_t s = grid_args(&g, ga);
+    h3f_status_t s = grid_args(&g, rows, ga);
     if (s != H3F_OK) return s;
     const int64_t blocks = (rows + 255) / 256;
-    if (blocks > 0x7fffffff) return H3F_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(positions_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), pos, rows, ga);
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
@@ -287,7 +294,7 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
         (rope->d_t % (2 * V) || rope->d_h % (2 * V) || rope->d_w % (2 * V)))
         return H3F_ERR_UNSUPPORTED;
     if (!(rope->theta > 0.0)) return H3F_ERR_BAD_SHAPE;
-    if (rows > 0x7fffffff || (int64_t)heads * 2 > 0x7fffffff) return H3F_ERR_UNSUPPORTED;
+    if (rows > 0x7fffffff || heads > 0x3fffffff) return H3F_ERR_UNSUPPORTED;
     if (!aligned16(q_out) || !aligned16(k_out) || !aligned16(q) || !aligned16(k) ||
         !aligned16(q_weight) || !aligned16(k_weight))
         return H3F_ERR_MISALIGNED;
@@ -316,6 +323,15 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
     const Region rk = region(k, k_row_stride, k_head_stride);
     if (!rows_separate(rqo) || !rows_separate(rko) || !rows_separate(rq) || !rows_separate(rk))
         return H3F_ERR_BAD_STRIDE;
+    // One row's heads are addressed through a 32-bit buffer resource; slots past the
+    // last head reach at most 64 head strides beyond the row span.
+    {
+        const int64_t hs_max = (int64_t)head_dim * e +
+            (heads > 1 ? e * std::max(std::max(q_out_head_stride, k_out_head_stride),
+                                      std::max(q_head_stride, k_head_stride)) : 0);
+        const int64_t span_max = std::max(std::max(rqo.span, rko.span), std::max(rq.span, rk.span));
+        if (span_max + 64 * hs_max > 0xFFFFFFF0ll) return H3F_ERR_UNSUPPORTED;
+    }
     const Region rw1 = region2d(q_weight, 1, head_dim, head_dim, e);
     const Region rw2 = region2d(k_weight, 1, head_dim, head_dim, e);
     // q_out: may be q exactly; must not touch k, k_out or the weights.
@@ -332,28 +348,33 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
         return H3F_ERR_ALIASING;
 
     QKArgs a{};
-    a.q_out = q_out;
-    a.qo_rs = q_out_row_stride;
-    a.qo_hs = q_out_head_stride;
-    a.k_out = k_out;
-    a.ko_rs = k_out_row_stride;
-    a.ko_hs = k_out_head_stride;
-    a.q = q;
-    a.q_rs = q_row_stride;
-    a.q_hs = q_head_stride;
-    a.k = k;
-    a.k_rs = k_row_stride;
-    a.k_hs = k_head_stride;
-    a.qw = q_weight;
-    a.kw = k_weight;
-    a.rows = rows;
-    a.heads = heads;
+    a.q_out = static_cast<char*>(q_out);
+    a.qo_rs = q_out_row_stride * e;
+    a.qo_hs = (heads > 1 ? q_out_head_stride : head_dim) * e;
+    a.k_out = static_cast<char*>(k_out);
+    a.ko_rs = k_out_row_stride * e;
+    a.ko_hs = (heads > 1 ? k_out_head_stride : head_dim) * e;
+    a.q = static_cast<const char*>(q);
+    a.q_rs = q_row_stride * e;
+    a.q_hs = (heads > 1 ? q_head_stride : head_dim) * e;
+    a.k = static_cast<const char*>(k);
+    a.k_rs = k_row_stride * e;
+    a.k_hs = (heads > 1 ? k_head_stride : head_dim) * e;
+    a.qo_span = (uint32_t)rqo.span;
+    a.ko_span = (uint32_t)rko.span;
+    a.q_span = (uint32_t)rq.span;
+    a.k_span = (uint32_t)rk.span;
+    a.qw = static_cast<const char*>(q_weight);
+    a.kw = static_cast<const char*>(k_weight);
+    const int gpw = 64 / lph;
+    a.nl = (heads + gpw - 1) / gpw;
+    a.div_slots = make_fastdiv((uint32_t)(2 * a.nl));
     a.head_dim = head_dim;
     a.inv_head_dim = 1.0f / (float)head_dim;
     a.eps = eps;
     a.c1 = rope->d_t;
     a.c2 = rope->d_t + rope->d_h;
-    h3f_status_t s = grid_args(rope, a.grid);
+    h3f_status_t s = grid_args(rope, rows, a.grid);
     if (s != H3F_OK) return s;
     // Frequencies theta^(-2j/d_c), evaluated in double and rounded once to fp32.
     const int32_t dims[3] = {rope->d_t, rope->d_h, rope->d_w};
@@ -365,10 +386,10 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
     const bool half = rope->pairing == H3F_ROPE_HALF_SPLIT;
     hipError_t err;
     if (dtype == H3F_BF16)
-        err = half ? dispatch_lph<__bf16, 8, true>(a, lph, st)
-                   : dispatch_lph<__bf16, 8, false>(a, lph, st);
+        err = half ? dispatch_lph<__bf16, 8, true>(a, lph, rows, st)
+                   : dispatch_lph<__bf16, 8, false>(a, lph, rows, st);
     else
-        err = half ? dispatch_lph<float, 4, true>(a, lph, st)
-                   : dispatch_lph<float, 4, false>(a, lph, st);
+        err = half ? dispatch_lph<float, 4, true>(a, lph, rows, st)
+                   : dispatch_lph<float, 4, false>(a, lph, rows, st);
     return err == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }
