@@ -71,7 +71,7 @@ def op_bytes(name, N, c, x_bytes=2):
     raise KeyError(name)
 
 
-def source_digest(*names):
+def source_digest(names):
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "video_diffusion_transformer_h3f_amd", "csrc", n), "rb") as f:
@@ -79,18 +79,19 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_file, kernel_key, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when it is missing or the kernel source changed since it was taken."""
+def traffic_from_profiles(kernel_key, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/pmc_traffic.json), or None when it is missing or the kernel's
+    source changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         doc = json.load(open(path))
         ent = doc["kernels"][f"{kernel_key}@{workload}"]
-    except (KeyError, ValueError):
-        return None
-    if ent.get("source_digest") != source_digest(kernel_file):
+        if ent.get("source_digest") != source_digest(ent["source_files"]):
+            return None
+    except (KeyError, ValueError, OSError):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -268,10 +269,9 @@ def main():
                         "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
 
     dom = "swiglu"
-    kern_file = "k_elementwise.hip"
     roofline = {"bound": "hbm", "achieved": per_op[dom]["GBps"], "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": per_op[dom]["frac_of_peak"],
-                "traffic": traffic_from_profiles(kern_file, dom, args.workload),
+                "traffic": traffic_from_profiles(dom, args.workload),
                 "kernel": "swiglu_kernel<bf16,8>", "bytes_per_launch": per_op[dom]["bytes"],
                 "avg_launch_ms": per_op[dom]["avg_ms"]}
 

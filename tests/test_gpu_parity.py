@@ -411,3 +411,111 @@ def test_zero_rows_is_noop_and_errors_raise():
     with pytest.raises(h3.H3FError) as e:
         h3.h3f_gated_residual(x, x, torch.zeros(256, dtype=torch.bfloat16, device=DEV))
     assert e.value.name == "H3F_ERR_ALIASING"
+
+
+# ------------------------------------------------------------------------------------
+# 10 s shape and the roofline sweep, sampled rows
+# ------------------------------------------------------------------------------------
+
+def _sampled_all_ops(c, every=97):
+    N, D, F, H, Dh = n_tokens(c), c["D"], c["F"], c["heads"], c["Dh"]
+    idx = sample_rows(N, N - c["A"], every=every)
+    x = dev_tensor("x", N, D, "bf16")
+    sh, sc, gt = (dev_tensor(n, 1, D, "bf16") for n in ("shift", "scale", "gate"))
+    y = torch.empty_like(x)
+    h3.h3f_adaln_modulate(y, x, sh, sc)
+    assert_close(rows_of(y, idx), oracle.adaln_modulate(
+        host("x", idx, D, "bf16"), host("shift", 1, D, "bf16"), host("scale", 1, D, "bf16")),
+        "bf16", "adaln")
+    del y
+    h = dev_tensor("h", N, D, "bf16")
+    h3.h3f_gated_residual(x, h, gt)
+    assert_close(rows_of(x, idx), oracle.gated_residual(
+        host("x", idx, D, "bf16"), host("h", idx, D, "bf16"), host("gate", 1, D, "bf16")),
+        "bf16", "gated")
+    del x, h
+    gu = dev_tensor("gate_up", N, 2 * F, "bf16")
+    act = torch.empty(N, F, dtype=torch.bfloat16, device=DEV)
+    h3.h3f_swiglu(act, gu)
+    assert_close(rows_of(act, idx), oracle.swiglu(host("gate_up", idx, 2 * F, "bf16")), "bf16",
+                 "swiglu")
+    del gu, act
+    q = dev_tensor("q", N, H * Dh, "bf16").view(N, H, Dh)
+    k = dev_tensor("k", N, H * Dh, "bf16").view(N, H, Dh)
+    qw = dev_tensor("q_weight", 1, Dh, "bf16").view(Dh)
+    kw = dev_tensor("k_weight", 1, Dh, "bf16").view(Dh)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    h3.h3f_qk_rmsnorm_rope3d(qo, ko, q, k, qw, kw,
+                             h3.make_rope(c["T"], c["H"], c["W"], c["A"], c["split"]))
+    pos = oracle.positions(N, c["T"], c["H"], c["W"], c["A"])[idx]
+    rq, rk = oracle.qk_rmsnorm_rope3d(host("q", idx, H * Dh, "bf16").reshape(-1, H, Dh),
+                                      host("k", idx, H * Dh, "bf16").reshape(-1, H, Dh),
+                                      to_np(qw), to_np(kw), pos, c["split"])
+    assert_close(rows_of(qo, idx), rq, "bf16", "q")
+    assert_close(rows_of(ko, idx), rk, "bf16", "k")
+
+
+def test_full_10s_shape_all_ops_sampled():
+    _sampled_all_ops(S10, every=211)
+
+
+@pytest.mark.parametrize("D,F", [(3072, 8320), (4096, 11008), (6144, 16640)])
+def test_sweep_shapes_all_ops_sampled(D, F):
+    _sampled_all_ops(dict(T=8, H=48, W=84, A=512, D=D, heads=D // 128, Dh=128,
+                          split=(32, 48, 48), F=F), every=389)
+
+
+# ------------------------------------------------------------------------------------
+# block epilogue chain: 10 s shape, fp32 residual stream, packed qkv, 50 steps
+# ------------------------------------------------------------------------------------
+
+def test_chain_10s_50_steps_sampled():
+    c = S10
+    N, D, F, H, Dh = n_tokens(c), c["D"], c["F"], c["heads"], c["Dh"]
+    steps = 50
+    x = dev_tensor("x", N, D, "f32")
+    mods = {n: dev_tensor(n, 1, D, "f32") for n in
+            ("shift", "scale", "gate", "shift2", "scale2", "gate2")}
+    h1 = dev_tensor("h", N, D, "bf16")
+    h2 = dev_tensor("h2", N, D, "bf16")
+    gu = dev_tensor("gate_up", N, 2 * F, "bf16")
+    qkv = torch.empty(N, 3, H, Dh, dtype=torch.bfloat16, device=DEV)
+    flat = qkv.view(N, 3 * H * Dh)
+    for i, n in enumerate(("q", "k", "v")):
+        h3gen.fill_device(flat[:, i * H * Dh:(i + 1) * H * Dh], n)
+    qw = dev_tensor("q_weight", 1, Dh, "bf16").view(Dh)
+    kw = dev_tensor("k_weight", 1, Dh, "bf16").view(Dh)
+    y = torch.empty(N, D, dtype=torch.bfloat16, device=DEV)
+    qo = torch.empty(N, H, Dh, dtype=torch.bfloat16, device=DEV)
+    ko = torch.empty_like(qo)
+    act = torch.empty(N, F, dtype=torch.bfloat16, device=DEV)
+    rope = h3.make_rope(c["T"], c["H"], c["W"], c["A"], c["split"])
+    for _ in range(steps):
+        h3.h3f_adaln_modulate(y, x, mods["shift"], mods["scale"])
+        h3.h3f_qk_rmsnorm_rope3d(qo, ko, qkv[:, 0], qkv[:, 1], qw, kw, rope)
+        h3.h3f_gated_residual(x, h1, mods["gate"])
+        h3.h3f_adaln_modulate(y, x, mods["shift2"], mods["scale2"])
+        h3.h3f_swiglu(act, gu)
+        h3.h3f_gated_residual(x, h2, mods["gate2"])
+    torch.cuda.synchronize()
+
+    idx = sample_rows(N, N - c["A"], every=1999, head=16, tail=16)
+    hm = {n: host(n, 1, D, "f32") for n in mods}
+    rx = host("x", idx, D, "f32")
+    rh1, rh2 = host("h", idx, D, "bf16"), host("h2", idx, D, "bf16")
+    for _ in range(steps):
+        oracle.adaln_modulate(rx, hm["shift"], hm["scale"], y_dtype=np.uint16)
+        rx = oracle.gated_residual(rx, rh1, hm["gate"])
+        ry = oracle.adaln_modulate(rx, hm["shift2"], hm["scale2"], y_dtype=np.uint16)
+        rx = oracle.gated_residual(rx, rh2, hm["gate2"])
+    # x grows to ~ x0 + 50 (g1 h1 + g2 h2): std ~ 35; fp32 tolerance still applies
+    assert_close(rows_of(x, idx), rx, "f32", "chain x after 50 steps")
+    assert_close(rows_of(y, idx), ry, "bf16", "chain last adaln")
+    assert_close(rows_of(act, idx), oracle.swiglu(host("gate_up", idx, 2 * F, "bf16")), "bf16",
+                 "chain swiglu")
+    pos = oracle.positions(N, c["T"], c["H"], c["W"], c["A"])[idx]
+    rq, rk = oracle.qk_rmsnorm_rope3d(host("q", idx, H * Dh, "bf16").reshape(-1, H, Dh),
+                                      host("k", idx, H * Dh, "bf16").reshape(-1, H, Dh),
+                                      to_np(qw), to_np(kw), pos, c["split"])
+    assert_close(rows_of(qo, idx), rq, "bf16", "chain q")
+    assert_close(rows_of(ko, idx), rk, "bf16", "chain k")
