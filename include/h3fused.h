@@ -23,9 +23,9 @@
  *     keeps no pointer after a call returns and allocates nothing.
  *   - Tensors are row-major with unit inner stride; every *_row_stride /
  *     *_head_stride / *_group_stride is in ELEMENTS of that tensor's type.
- *   - Vector width: 8 elements when any tensor of the call is bf16, else 4
- *     elements (fp32 only).  hidden / inner / head_dim and every stride must
- *     be multiples of it, and every pointer must be 16-byte aligned.
+ *   - Vector width: 4 elements when any tensor of the call is fp32, 8 elements
+ *     when all are bf16.  hidden / inner / head_dim and every stride must be
+ *     multiples of it, and every pointer must be 16-byte aligned.
  *   - Arithmetic is fp32 whatever the storage type; each output element is
  *     rounded once (round to nearest even) to its storage type.
  *   - Modulation vectors (shift, scale, gate) are [groups, hidden] rows: token

@@ -9,6 +9,7 @@
 namespace h3f {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -87,76 +88,83 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 
 // ---------------------------------------------------------------------------
 // Vec<T, N>: N consecutive elements of storage type T (float or __bf16) held
-// as raw 16-byte quads; widened to fp32 on use, narrowed with one
-// round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950) on store.
+// raw (whole 16-byte quads, or one 8-byte pair for 4 bf16 next to fp32
+// streams); widened to fp32 on use, narrowed with one round-to-nearest-even
+// (v_cvt_pk_bf16_f32 on gfx950) on store.
 // ---------------------------------------------------------------------------
 template <typename T, int N>
 struct Vec {
-    static constexpr int kQuads = N * (int)sizeof(T) / 16;
-    static_assert(kQuads >= 1 && N * (int)sizeof(T) % 16 == 0, "vector must be whole 16-byte quads");
-    u32x4 q[kQuads];
+    static constexpr int kBytes = N * (int)sizeof(T);
+    static_assert(kBytes == 8 || (kBytes >= 16 && kBytes % 16 == 0),
+                  "vector must be 8 bytes or whole 16-byte quads");
+    static constexpr int kQuads = kBytes / 16;  // 0 for an 8-byte vector
+    static constexpr int kWords = kBytes / 4;
+    u32x4 q[kQuads > 0 ? kQuads : 1];  // an 8-byte vector uses q[0].xy
+
+    __device__ __forceinline__ unsigned word(int i) const { return q[i / 4][i % 4]; }
+    __device__ __forceinline__ void set_word(int i, unsigned v) { q[i / 4][i % 4] = v; }
 
     template <bool NT>
     __device__ __forceinline__ void load(const T* p) {
+        if constexpr (kBytes == 8) {
+            const u32x2 v = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p))
+                               : *reinterpret_cast<const u32x2*>(p);
+            q[0][0] = v[0];
+            q[0][1] = v[1];
+        } else {
 #pragma unroll
-        for (int i = 0; i < kQuads; ++i)
-            q[i] = NT ? ld16_nt(p + i * (16 / (int)sizeof(T))) : ld16(p + i * (16 / (int)sizeof(T)));
-    }
-    template <bool NT>
-    __device__ __forceinline__ void store(T* p) const {
-#pragma unroll
-        for (int i = 0; i < kQuads; ++i) {
-            if (NT)
-                st16_nt(p + i * (16 / (int)sizeof(T)), q[i]);
-            else
-                st16(p + i * (16 / (int)sizeof(T)), q[i]);
+            for (int i = 0; i < kQuads; ++i)
+                q[i] = NT ? ld16_nt(p + i * (16 / (int)sizeof(T))) : ld16(p + i * (16 / (int)sizeof(T)));
         }
     }
     // Buffer forms: byte offset of the first element inside the resource.
     template <int AUX>
     __device__ __forceinline__ void load_buf(rsrc_t r, uint32_t off) {
+        if constexpr (kBytes == 8) {
+            const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+            q[0][0] = v[0];
+            q[0][1] = v[1];
+        } else {
 #pragma unroll
-        for (int i = 0; i < kQuads; ++i) q[i] = buf_ld<AUX>(r, off + 16u * i);
+            for (int i = 0; i < kQuads; ++i) q[i] = buf_ld<AUX>(r, off + 16u * i);
+        }
     }
     template <int AUX>
     __device__ __forceinline__ void store_buf(rsrc_t r, uint32_t off) const {
+        if constexpr (kBytes == 8) {
+            const u32x2 v = {q[0][0], q[0][1]};
+            __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, AUX);
+        } else {
 #pragma unroll
-        for (int i = 0; i < kQuads; ++i) buf_st<AUX>(r, off + 16u * i, q[i]);
+            for (int i = 0; i < kQuads; ++i) buf_st<AUX>(r, off + 16u * i, q[i]);
+        }
     }
     __device__ __forceinline__ void zero() {
 #pragma unroll
-        for (int i = 0; i < kQuads; ++i) q[i] = u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < (kQuads > 0 ? kQuads : 1); ++i) q[i] = u32x4{0u, 0u, 0u, 0u};
     }
     __device__ __forceinline__ void to_float(float (&f)[N]) const {
         if constexpr (sizeof(T) == 4) {
 #pragma unroll
-            for (int i = 0; i < kQuads; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) f[4 * i + j] = __uint_as_float(q[i][j]);
+            for (int i = 0; i < kWords; ++i) f[i] = __uint_as_float(word(i));
         } else {
 #pragma unroll
-            for (int i = 0; i < kQuads; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f[8 * i + 2 * j] = __uint_as_float(q[i][j] << 16);
-                    f[8 * i + 2 * j + 1] = __uint_as_float(q[i][j] & 0xffff0000u);
-                }
+            for (int i = 0; i < kWords; ++i) {
+                f[2 * i] = __uint_as_float(word(i) << 16);
+                f[2 * i + 1] = __uint_as_float(word(i) & 0xffff0000u);
+            }
         }
     }
     __device__ __forceinline__ void from_float(const float (&f)[N]) {
         if constexpr (sizeof(T) == 4) {
 #pragma unroll
-            for (int i = 0; i < kQuads; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) q[i][j] = __float_as_uint(f[4 * i + j]);
+            for (int i = 0; i < kWords; ++i) set_word(i, __float_as_uint(f[i]));
         } else {
 #pragma unroll
-            for (int i = 0; i < kQuads; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x2 v = {f[8 * i + 2 * j], f[8 * i + 2 * j + 1]};
-                    q[i][j] = __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
-                }
+            for (int i = 0; i < kWords; ++i) {
+                const f32x2 v = {f[2 * i], f[2 * i + 1]};
+                set_word(i, __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2)));
+            }
         }
     }
 };

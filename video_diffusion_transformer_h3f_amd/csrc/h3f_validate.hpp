@@ -12,9 +12,10 @@ namespace h3f {
 inline int dtype_bytes(h3f_dtype_t t) { return t == H3F_BF16 ? 2 : 4; }
 inline bool dtype_ok(int t) { return t == H3F_F32 || t == H3F_BF16; }
 
-// Elements per 16-byte-aligned vector chunk: 8 when any tensor of the call is
-// bf16, else 4.
-inline int vec_width(bool any_bf16) { return any_bf16 ? 8 : 4; }
+// Elements per lane chunk: 4 when any tensor of the call is fp32 (one 16-byte
+// quad of fp32; bf16 streams then move 8 bytes per lane), 8 when all are bf16.
+// Every load / store instruction of a wavefront is then contiguous.
+inline int vec_width(bool any_f32) { return any_f32 ? 4 : 8; }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -205,12 +205,10 @@ h3f_status_t dispatch(const AdalnArgs& a, int max_nv, bool single_group, hipStre
     return e == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }
 
-// Largest hidden size held in registers: 32 chunks of 8 bf16, 16 chunks of 8
-// fp32 (mixed) or 32 chunks of 4 fp32.
+// Largest hidden size held in registers: 32 chunks per lane of 8 bf16 or of 4
+// fp32 (x fp32 always uses 4-element chunks).
 inline int64_t max_hidden(h3f_dtype_t x_dtype) { return x_dtype == H3F_BF16 ? 16384 : 8192; }
-inline int max_nv_for(h3f_dtype_t x_dtype, int V) {
-    return x_dtype == H3F_BF16 ? 32 : (V == 8 ? 16 : 32);
-}
+inline int max_nv_for(h3f_dtype_t, int) { return 32; }
 
 h3f_status_t check_mod(const void* p, int64_t groups, int64_t gs, int64_t hidden, int V) {
     if (!aligned16(p)) return H3F_ERR_MISALIGNED;
@@ -235,7 +233,7 @@ extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t
     if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return H3F_ERR_BAD_DTYPE;
     if (x_dtype == H3F_BF16 && y_dtype == H3F_F32) return H3F_ERR_BAD_DTYPE;
     if (rows < 0 || hidden <= 0 || rows_per_group < 1) return H3F_ERR_BAD_SHAPE;
-    const int V = vec_width(x_dtype == H3F_BF16 || y_dtype == H3F_BF16);
+    const int V = vec_width(x_dtype == H3F_F32 || y_dtype == H3F_F32);
     if (hidden % V) return H3F_ERR_BAD_SHAPE;
     if (hidden > max_hidden(x_dtype) || rows > 0x7fffffff) return H3F_ERR_UNSUPPORTED;
     if (!aligned16(y) || !aligned16(x)) return H3F_ERR_MISALIGNED;
@@ -275,7 +273,7 @@ extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t
         return dispatch<float, float, float, 4, false>(a, mnv, one, st);
     if (x_dtype == H3F_BF16)
         return dispatch<__bf16, __bf16, __bf16, 8, false>(a, mnv, one, st);
-    return dispatch<float, __bf16, float, 8, false>(a, mnv, one, st);
+    return dispatch<float, __bf16, float, 4, false>(a, mnv, one, st);
 }
 
 extern "C" h3f_status_t h3f_gated_residual_adaln(
@@ -289,7 +287,7 @@ extern "C" h3f_status_t h3f_gated_residual_adaln(
     if (x_dtype == H3F_BF16 && (h_dtype == H3F_F32 || y_dtype == H3F_F32))
         return H3F_ERR_BAD_DTYPE;
     if (rows < 0 || hidden <= 0 || rows_per_group < 1) return H3F_ERR_BAD_SHAPE;
-    const int V = vec_width(x_dtype == H3F_BF16 || h_dtype == H3F_BF16 || y_dtype == H3F_BF16);
+    const int V = vec_width(x_dtype == H3F_F32 || h_dtype == H3F_F32 || y_dtype == H3F_F32);
     if (hidden % V) return H3F_ERR_BAD_SHAPE;
     if (hidden > max_hidden(x_dtype) || rows > 0x7fffffff) return H3F_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(h) || !aligned16(y)) return H3F_ERR_MISALIGNED;
@@ -340,7 +338,7 @@ extern "C" h3f_status_t h3f_gated_residual_adaln(
     if (x_dtype == H3F_BF16) return dispatch<__bf16, __bf16, __bf16, 8, true>(a, mnv, one, st);
     if (h_dtype == H3F_F32 && y_dtype == H3F_F32)
         return dispatch<float, float, float, 4, true>(a, mnv, one, st);
-    if (h_dtype == H3F_F32) return dispatch<float, __bf16, float, 8, true>(a, mnv, one, st);
-    if (y_dtype == H3F_F32) return dispatch<float, float, __bf16, 8, true>(a, mnv, one, st);
-    return dispatch<float, __bf16, __bf16, 8, true>(a, mnv, one, st);
+    if (h_dtype == H3F_F32) return dispatch<float, __bf16, float, 4, true>(a, mnv, one, st);
+    if (y_dtype == H3F_F32) return dispatch<float, float, __bf16, 4, true>(a, mnv, one, st);
+    return dispatch<float, __bf16, __bf16, 4, true>(a, mnv, one, st);
 }

@@ -248,7 +248,7 @@ extern "C" h3f_status_t h3f_gated_residual(void* x, h3f_dtype_t x_dtype, int64_t
     if (x_dtype == H3F_BF16 && h_dtype == H3F_F32) return H3F_ERR_BAD_DTYPE;
     if (rows < 0 || hidden <= 0 || rows_per_group < 1) return H3F_ERR_BAD_SHAPE;
     if (rows > 0x7fffffff) return H3F_ERR_UNSUPPORTED;
-    const int V = vec_width(x_dtype == H3F_BF16 || h_dtype == H3F_BF16);
+    const int V = vec_width(x_dtype == H3F_F32 || h_dtype == H3F_F32);
     if (hidden % V) return H3F_ERR_BAD_SHAPE;
     if (hidden / V > 0x7fffffff) return H3F_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(h) || !aligned16(gate)) return H3F_ERR_MISALIGNED;
@@ -272,7 +272,7 @@ extern "C" h3f_status_t h3f_gated_residual(void* x, h3f_dtype_t x_dtype, int64_t
     if (x_dtype == H3F_BF16)
         return launch_gated<__bf16, __bf16, 8>(x, xs, h, hs, gate, gs, rows_per_group, rows,
                                                hidden, st);
-    return launch_gated<float, __bf16, 8>(x, xs, h, hs, gate, gs, rows_per_group, rows, hidden,
+    return launch_gated<float, __bf16, 4>(x, xs, h, hs, gate, gs, rows_per_group, rows, hidden,
                                           st);
 }
 
@@ -283,7 +283,7 @@ extern "C" h3f_status_t h3f_swiglu(void* out, int64_t out_row_stride, const void
     if (!out || !a || !b) return H3F_ERR_NULL_POINTER;
     if (!dtype_ok(dtype)) return H3F_ERR_BAD_DTYPE;
     if (rows < 0 || inner <= 0) return H3F_ERR_BAD_SHAPE;
-    const int V = vec_width(dtype == H3F_BF16);
+    const int V = vec_width(dtype == H3F_F32);
     if (inner % V) return H3F_ERR_BAD_SHAPE;
     if (inner / V > 0x7fffffff) return H3F_ERR_UNSUPPORTED;
     if (!aligned16(out) || !aligned16(a) || !aligned16(b)) return H3F_ERR_MISALIGNED;

@@ -281,7 +281,7 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
         return H3F_ERR_NULL_POINTER;
     if (!dtype_ok(dtype)) return H3F_ERR_BAD_DTYPE;
     if (rows < 0 || heads < 1 || head_dim < 1) return H3F_ERR_BAD_SHAPE;
-    const int V = vec_width(dtype == H3F_BF16);
+    const int V = vec_width(dtype == H3F_F32);
     if (head_dim % V) return H3F_ERR_BAD_SHAPE;
     const int lph = head_dim / V;
     if (lph < 2 || lph > 64 || (lph & (lph - 1))) return H3F_ERR_UNSUPPORTED;
