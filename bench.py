@@ -268,6 +268,31 @@ def main():
         per_op[name] = {"avg_ms": round(avg, 4), "bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1),
                         "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
 
+    # Step-reuse test (residual difference between neighbouring steps): timed on its
+    # own, outside the block step, since a block runs it at most once per step.
+    extra_ops = {}
+    if not chain:
+        x_prev = torch.empty_like(t["x"])
+        h3gen.fill_device(x_prev, "x_prev")
+        l1_out = torch.zeros(3, dtype=torch.float64, device=dev)
+        ws = torch.empty(max(16, h3.h3f_residual_l1_workspace_bytes(N, c["D"], t["x"].dtype)),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            h3.h3f_residual_l1(l1_out, t["x"], x_prev, ws)
+        torch.cuda.synchronize()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record()
+        for _ in range(K):
+            h3.h3f_residual_l1(l1_out, t["x"], x_prev, ws)
+        r1.record()
+        torch.cuda.synchronize()
+        avg = r0.elapsed_time(r1) / K
+        b = 2 * N * c["D"] * 2
+        extra_ops["residual_l1"] = {"avg_ms": round(avg, 4), "bytes": b,
+                                    "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+                                    "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del x_prev, ws
+
     dom = "swiglu"
     roofline = {"bound": "hbm", "achieved": per_op[dom]["GBps"], "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": per_op[dom]["frac_of_peak"],
@@ -307,6 +332,7 @@ def main():
         "config": config,
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
         "per_op": per_op,
+        "extra_ops": extra_ops,
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "wall_s_timed_region": round(wall, 4),
         "roofline": roofline,

@@ -67,7 +67,8 @@ typedef enum {
     H3F_ERR_BAD_DTYPE = 5,
     H3F_ERR_ALIASING = 6,
     H3F_ERR_LAUNCH = 7,
-    H3F_ERR_UNSUPPORTED = 8
+    H3F_ERR_UNSUPPORTED = 8,
+    H3F_ERR_WORKSPACE = 9
 } h3f_status_t;
 
 /* RoPE pair layouts inside one axis chunk of size d_c */
@@ -200,6 +201,30 @@ h3f_status_t h3f_gated_residual_adaln(void* x, h3f_dtype_t x_dtype, int64_t x_ro
                                       int64_t mod_group_stride, int64_t rows_per_group,
                                       void* y, h3f_dtype_t y_dtype, int64_t y_row_stride,
                                       int64_t rows, int64_t hidden, float eps, void* stream);
+
+/*
+ * Residual difference between neighbouring denoising steps, the reuse test of
+ * step caching (the report page's Cache-DiT paragraph, section "Só com três
+ * camadas…": reuse when a residual difference is under a threshold such as
+ * 0.04 or 0.08; the page gives no formula -- the relative L1 distance is the
+ * reading used here):
+ *   out[0] = sum |cur - prev|,  out[1] = sum |prev|,  out[2] = out[0] / out[1]
+ * over all [rows, hidden] elements.  out: device double[3].  cur, prev:
+ * [rows, hidden] of dtype with their own row strides.  Deterministic: fixed
+ * partition, fp32 sums inside a workgroup, fp64 across workgroups in index
+ * order (bit-identical run to run).  workspace: device scratch of at least
+ * h3f_residual_l1_workspace_bytes(rows, hidden, dtype) bytes, 16-byte aligned,
+ * owned by the caller, contents need no initialisation; calls that share a
+ * workspace must be ordered on one stream.  Unlike the operators, rows == 0
+ * is rejected (H3F_ERR_BAD_SHAPE): an empty tensor has no relative
+ * difference.  If sum |prev| is 0, out[2] is inf or NaN (IEEE division).
+ * Returns 0 from the size query for an invalid shape or type.
+ */
+size_t h3f_residual_l1_workspace_bytes(int64_t rows, int64_t hidden, h3f_dtype_t dtype);
+h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cur_row_stride,
+                             const void* prev, int64_t prev_row_stride, h3f_dtype_t dtype,
+                             int64_t rows, int64_t hidden, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * Streaming copy (measurement helper, not an operator): dst[0:bytes) =

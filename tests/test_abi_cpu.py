@@ -14,14 +14,14 @@ import video_diffusion_transformer_h3f_amd as h3
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "h3fused.h")
 
-OK, NULLP, SHAPE, STRIDE, MISAL, DTYPE, ALIAS, LAUNCH, UNSUP = range(9)
+OK, NULLP, SHAPE, STRIDE, MISAL, DTYPE, ALIAS, LAUNCH, UNSUP, WORKSPACE = range(10)
 F32, BF16 = 0, 1
 
 
 def declared():
     src = open(HEADER).read()
-    return set(re.findall(r"^\s*(?:h3f_status_t|int|const char\s*\*)\s*(h3f_\w+)\s*\(", src,
-                          re.M))
+    return set(re.findall(r"^\s*(?:h3f_status_t|int|size_t|const char\s*\*)\s*(h3f_\w+)\s*\(",
+                          src, re.M))
 
 
 def test_header_declares_the_binding_exports():
@@ -41,7 +41,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_status_strings():
     L = h3.lib()
-    for s in range(9):
+    for s in range(10):
         assert L.h3f_status_string(s)
     assert L.h3f_status_string(99) == b"unknown status"
 
@@ -227,3 +227,31 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(4, 8)
     with pytest.raises(ValueError):
         h3.h3f_gated_residual(x, x, x[0])
+
+
+# --- residual difference (step-reuse test) --------------------------------------------------
+
+def test_residual_l1_validation():
+    L.h3f_residual_l1_workspace_bytes.restype = ctypes.c_size_t
+    need = L.h3f_residual_l1_workspace_bytes(125120, 5120, BF16)
+    assert need > 0 and need % 16 == 0
+    assert L.h3f_residual_l1_workspace_bytes(0, 5120, BF16) == 0
+    assert L.h3f_residual_l1_workspace_bytes(4, 5121, BF16) == 0
+
+    def l1(out=A(0), cur=A(1), cs=512, prev=A(2), ps=512, dt=BF16, rows=4, hidden=512, ws=A(3),
+           wsb=1 << 20):
+        return L.h3f_residual_l1(out, cur, cs, prev, ps, dt, rows, hidden, ws, wsb, None)
+
+    assert l1(out=None) == NULLP
+    assert l1(rows=0) == SHAPE
+    assert l1(prev=None) == NULLP
+    assert l1(dt=4) == DTYPE
+    assert l1(hidden=500) == SHAPE
+    assert l1(cur=P(0x20000008)) == MISAL
+    assert l1(out=P(0x10000004)) == MISAL
+    assert l1(cs=256) == STRIDE
+    assert l1(ws=None) == WORKSPACE
+    assert l1(wsb=8) == WORKSPACE
+    assert l1(ws=P(0x40000008)) == WORKSPACE
+    assert l1(ws=A(1)) == ALIAS
+    assert l1(out=A(2)) == ALIAS

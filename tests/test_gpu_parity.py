@@ -519,3 +519,40 @@ def test_chain_10s_50_steps_sampled():
                                       to_np(qw), to_np(kw), pos, c["split"])
     assert_close(rows_of(qo, idx), rq, "bf16", "chain q")
     assert_close(rows_of(ko, idx), rk, "bf16", "chain k")
+
+
+# ------------------------------------------------------------------------------------
+# residual difference (step-reuse test): a global reduction, compared as a whole
+# ------------------------------------------------------------------------------------
+
+# fp32 lane sums of 64 terms, a 6-level DPP tree and two fp32 workgroup levels before
+# fp64: relative error below ~72 * 2^-24 of the sum of |terms|; 1e-5 leaves margin.
+L1_RTOL = 1e-5
+
+
+def _l1_check(rows, D, dt, rs_pad=0):
+    cur = dev_tensor("x", rows, D, dt, row_stride=D + rs_pad)
+    prev = dev_tensor("x_prev", rows, D, dt, row_stride=D + rs_pad)
+    out = torch.zeros(3, dtype=torch.float64, device=DEV)
+    h3.h3f_residual_l1(out, cur, prev)
+    got = out.cpu().numpy()
+    num, den = oracle.residual_l1(host("x", rows, D, dt), host("x_prev", rows, D, dt))
+    assert abs(got[0] - num) <= L1_RTOL * num
+    assert abs(got[1] - den) <= L1_RTOL * den
+    assert abs(got[2] - num / den) <= 2 * L1_RTOL * (num / den)
+    return out, cur, prev
+
+
+@pytest.mark.parametrize("rows,D,dt,pad", [(112, 256, "f32", 0), (1001, 5120, "bf16", 0),
+                                          (33, 1000, "bf16", 24), (3, 8, "bf16", 0)])
+def test_residual_l1(rows, D, dt, pad):
+    _l1_check(rows, D, dt, pad)
+
+
+def test_residual_l1_full_5s_shape_deterministic_and_zero():
+    out, cur, prev = _l1_check(n_tokens(S5), S5["D"], "bf16")
+    out2 = torch.zeros(3, dtype=torch.float64, device=DEV)
+    h3.h3f_residual_l1(out2, cur, prev)
+    assert torch.equal(out, out2)  # bit-identical run to run
+    h3.h3f_residual_l1(out2, prev, prev)
+    assert out2[0].item() == 0.0 and out2[2].item() == 0.0

@@ -24,13 +24,13 @@ H3F_ROPE_HALF_SPLIT = 1
 STATUS = {
     0: "H3F_OK", 1: "H3F_ERR_NULL_POINTER", 2: "H3F_ERR_BAD_SHAPE", 3: "H3F_ERR_BAD_STRIDE",
     4: "H3F_ERR_MISALIGNED", 5: "H3F_ERR_BAD_DTYPE", 6: "H3F_ERR_ALIASING", 7: "H3F_ERR_LAUNCH",
-    8: "H3F_ERR_UNSUPPORTED",
+    8: "H3F_ERR_UNSUPPORTED", 9: "H3F_ERR_WORKSPACE",
 }
 
 EXPORTS = [
     "h3f_abi_version", "h3f_status_string", "h3f_rope3d_positions", "h3f_adaln_modulate",
     "h3f_gated_residual", "h3f_swiglu", "h3f_qk_rmsnorm_rope3d", "h3f_gated_residual_adaln",
-    "h3f_stream_copy",
+    "h3f_stream_copy", "h3f_residual_l1_workspace_bytes", "h3f_residual_l1",
 ]
 
 
@@ -77,8 +77,11 @@ def lib():
         L.h3f_gated_residual_adaln.argtypes = [p, st, i64, p, st, i64, p, p, p, i64, i64, p, st,
                                                i64, i64, i64, f, p]
         L.h3f_stream_copy.argtypes = [p, p, i64, p]
+        L.h3f_residual_l1.argtypes = [p, p, i64, p, i64, st, i64, i64, p, ctypes.c_size_t, p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = st
+        L.h3f_residual_l1_workspace_bytes.argtypes = [i64, i64, st]
+        L.h3f_residual_l1_workspace_bytes.restype = ctypes.c_size_t
         _lib = L
     return _lib
 
@@ -290,6 +293,36 @@ def h3f_gated_residual_adaln(x, h, gate, shift, scale, y, eps: float = 1e-6,
         _ptr(x), _dtype(x), xs, _ptr(h), _dtype(h), hs, _ptr(gate), _ptr(shift), _ptr(scale), gs,
         rpg, _ptr(y), _dtype(y), ys, rows, hidden, eps, _stream(dev, stream)))
     return x, y
+
+
+def h3f_residual_l1_workspace_bytes(rows: int, hidden: int, dtype) -> int:
+    """Workspace bytes h3f_residual_l1 needs for a [rows, hidden] tensor of dtype."""
+    import torch
+
+    dt = H3F_BF16 if dtype == torch.bfloat16 else H3F_F32
+    return int(lib().h3f_residual_l1_workspace_bytes(rows, hidden, dt))
+
+
+def h3f_residual_l1(out, cur, prev, workspace=None, stream=None):
+    """out (float64 [3] on the GPU) = (sum|cur - prev|, sum|prev|, ratio).
+    workspace: uint8 GPU tensor of at least h3f_residual_l1_workspace_bytes();
+    allocated here (torch) when None."""
+    import torch
+
+    dev = _dev(out, cur, prev)
+    if out.dtype != torch.float64 or out.numel() < 3 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float64 tensor of >= 3 elements")
+    rows, hidden, cs = _rows2d(cur, "cur")
+    pr, ph, ps = _rows2d(prev, "prev")
+    if (pr, ph) != (rows, hidden) or cur.dtype != prev.dtype:
+        raise ValueError("cur and prev must share shape and dtype")
+    need = h3f_residual_l1_workspace_bytes(rows, hidden, cur.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check("h3f_residual_l1", lib().h3f_residual_l1(
+        _ptr(out), _ptr(cur), cs, _ptr(prev), ps, _dtype(cur), rows, hidden, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev, stream)))
+    return out
 
 
 def h3f_stream_copy(dst, src, stream=None):

@@ -14,6 +14,7 @@ extern "C" const char* h3f_status_string(h3f_status_t status) {
         case H3F_ERR_ALIASING: return "output overlaps another tensor of the call";
         case H3F_ERR_LAUNCH: return "kernel launch failed";
         case H3F_ERR_UNSUPPORTED: return "size or layout outside the supported range";
+        case H3F_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     }
     return "unknown status";
 }
