@@ -48,9 +48,10 @@ struct QKArgs {
     uint32_t qo_span, ko_span, q_span, k_span;  // bytes of one row's heads
     const char* qw;
     const char* kw;
-    int64_t row0;      // first row of this launch
-    FastDiv div_slots; // 2 * nl slots per token
-    int32_t nl;        // loads per tensor per token
+    int64_t row0;         // first row of this launch
+    uint32_t n_q_blocks;  // rows of this launch * nl: blocks [0, n) are q, [n, 2n) are k
+    FastDiv div_nl;       // nl slots per tensor per token
+    int32_t nl;           // loads per tensor per token
     int32_t head_dim;
     float inv_head_dim;
     float eps;
@@ -93,13 +94,16 @@ __global__ void __launch_bounds__(64) qk_rmsnorm_rope3d_kernel(QKArgs a) {
     const int gsub = lane / LPH;        // head-row slot of this lane
     const int e0 = (lane % LPH) * VEC;  // first element of the lane in its head
 
-    // Which token and which slot: wave-uniform.
+    // Which tensor, token and slot: wave-uniform.  Tensor-major order (every q
+    // slot of the launch, then every k slot) keeps one input and one output
+    // stream live at a time; interleaving q and k per token measured ~5% slower.
     const uint32_t bid = blockIdx.x;
-    const uint32_t rr = fdiv(bid, a.div_slots);
-    const uint32_t slot = bid - rr * a.div_slots.d;
+    const bool isk = bid >= a.n_q_blocks;
+    const uint32_t bb = isk ? bid - a.n_q_blocks : bid;
+    const uint32_t rr = fdiv(bb, a.div_nl);
+    const uint32_t slot = bb - rr * (uint32_t)a.nl;
     const int64_t row = a.row0 + rr;
-    const bool isk = slot >= (uint32_t)a.nl;
-    const uint32_t hd = (isk ? slot - a.nl : slot) * GPW + gsub;
+    const uint32_t hd = slot * GPW + gsub;
 
     // One 16-byte chunk per lane; a head slot past the last head lies outside the
     // row's resource (offset >= heads * head_stride >= span): reads 0, not stored.
@@ -197,11 +201,12 @@ __global__ void __launch_bounds__(256) positions_kernel(int32_t* __restrict__ po
 
 template <typename T, int VEC, int LPH, bool HALF>
 hipError_t launch_lph(QKArgs a, int64_t rows, hipStream_t st) {
-    const int64_t slots = a.div_slots.d;
+    const int64_t slots = 2 * (int64_t)a.nl;
     const int64_t step = 0x7fffffffll / slots;
     for (int64_t r0 = 0; r0 < rows; r0 += step) {
         const int64_t nr = rows - r0 < step ? rows - r0 : step;
         a.row0 = r0;
+        a.n_q_blocks = (uint32_t)(nr * a.nl);
         hipLaunchKernelGGL((qk_rmsnorm_rope3d_kernel<T, VEC, LPH, HALF>),
                            dim3((unsigned)(nr * slots)), dim3(64), 0, st, a);
     }
@@ -368,7 +373,7 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
     a.kw = static_cast<const char*>(k_weight);
     const int gpw = 64 / lph;
     a.nl = (heads + gpw - 1) / gpw;
-    a.div_slots = make_fastdiv((uint32_t)(2 * a.nl));
+    a.div_nl = make_fastdiv((uint32_t)a.nl);
     a.head_dim = head_dim;
     a.inv_head_dim = 1.0f / (float)head_dim;
     a.eps = eps;
