@@ -74,6 +74,10 @@ def host_lib():
         L.h3gen_fill_rows_host.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_uint64,
                                            ctypes.c_uint64, ctypes.c_float, ctypes.c_float]
+        L.h3gen_fill_cols_host.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint64,
+                                           ctypes.c_float, ctypes.c_float]
         _host = L
     return _host
 
@@ -122,6 +126,18 @@ def host_rows(name: str, rows, cols: int, dtype: str = "bf16", seed: int = 0,
     host_lib().h3gen_fill_rows_host(out.ctypes.data_as(ctypes.c_void_p), dt,
                                     ids.ctypes.data_as(ctypes.c_void_p), ids.shape[0], cols,
                                     seed, tid, mu, sigma)
+    return out
+
+
+def host_cols(name: str, rows: int, cols: int, col0: int, ncols: int, dtype: str = "bf16",
+              seed: int = 0, mu=None, sigma=None) -> np.ndarray:
+    """Columns [col0, col0 + ncols) of rows 0..rows-1 of logical tensor `name`
+    ([*, cols]) as a dense [rows, ncols] numpy array."""
+    mu, sigma = _dist(name, mu, sigma)
+    dt = BF16 if dtype == "bf16" else F32
+    out = np.empty((int(rows), int(ncols)), dtype=np.uint16 if dt == BF16 else np.float32)
+    host_lib().h3gen_fill_cols_host(out.ctypes.data_as(ctypes.c_void_p), dt, 0, int(rows), cols,
+                                    col0, ncols, seed, TENSOR_IDS[name], mu, sigma)
     return out
 
 

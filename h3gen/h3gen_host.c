@@ -51,3 +51,24 @@ void h3gen_fill_rows_host(void* dst, int dtype, const int64_t* row_ids,
         }
     }
 }
+
+/* Fill columns [col0, col0 + ncols) of rows [row0, row0 + rows) of a logical
+ * [*, cols] tensor into a dense [rows, ncols] dst. */
+void h3gen_fill_cols_host(void* dst, int dtype, int64_t row0, int64_t rows,
+                          int64_t cols, int64_t col0, int64_t ncols,
+                          uint64_t seed, uint64_t tensor_id, float mu,
+                          float sigma) {
+    const uint64_t s = h3gen_stream(seed, tensor_id);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < ncols; ++c) {
+            const uint64_t i = (uint64_t)(row0 + r) * (uint64_t)cols + (uint64_t)(col0 + c);
+            float v = h3gen_unit(s, i) * sigma;
+            v = v + mu;
+            if (dtype == H3GEN_F32)
+                ((float*)dst)[r * ncols + c] = v;
+            else
+                ((uint16_t*)dst)[r * ncols + c] = h3gen_bf16_rne(v);
+        }
+    }
+}

@@ -85,6 +85,11 @@ def _declare(L):
     L.oracle_gated_residual_adaln.argtypes = [_p, _int, _p, _int, _p, _p, _int,
                                               _p, _p, _p, _i64, _i64, _i64, _f]
     L.oracle_residual_l1.argtypes = [_p, _p, _p, _int, _i64, _i64]
+    L.oracle_subblock_pool.argtypes = [_p, _p, _int, _i64, _i32, _i32, _i32]
+    L.oracle_subblock_scores.argtypes = [_p, _p, _p, _i32, _i64, _i64, _i32]
+    L.oracle_subblock_keep.argtypes = [_i64, _d, _i32, _i32]
+    L.oracle_subblock_keep.restype = _i64
+    L.oracle_subblock_select.argtypes = [_p, _p, _i32, _i64, _i64, _i64]
 
 
 def _dt(a: np.ndarray) -> int:
@@ -248,3 +253,53 @@ def residual_l1(cur, prev):
     out = np.zeros(2, dtype=np.float64)
     lib().oracle_residual_l1(_ptr(out), _ptr(cur), _ptr(prev), _dt(cur), rows, hidden)
     return float(out[0]), float(out[1])
+
+
+# --- block-sparse attention router ----------------------------------------------
+
+SUBBLOCK_FIRST_STEP = 10
+
+
+def subblock_pool(x, block):
+    """x [rows, heads, Dh] -> per-block means, float64 [heads, n_blocks, Dh]."""
+    x = np.ascontiguousarray(x)
+    rows, heads, Dh = x.shape
+    nb = (rows + block - 1) // block
+    out = np.zeros((heads, nb, Dh), dtype=np.float64)
+    lib().oracle_subblock_pool(_ptr(out), _ptr(x), _dt(x), rows, heads, Dh, block)
+    return out
+
+
+def subblock_scores(pq, pk):
+    """pq [heads, nbq, Dh], pk [heads, nbk, Dh] (float64) -> [heads, nbq, nbk] float64."""
+    pq = np.ascontiguousarray(pq, dtype=np.float64)
+    pk = np.ascontiguousarray(pk, dtype=np.float64)
+    heads, nbq, Dh = pq.shape
+    assert pk.shape[0] == heads and pk.shape[2] == Dh
+    nbk = pk.shape[1]
+    out = np.zeros((heads, nbq, nbk), dtype=np.float64)
+    lib().oracle_subblock_scores(_ptr(out), _ptr(pq), _ptr(pk), heads, nbq, nbk, Dh)
+    return out
+
+
+def subblock_keep(n_blocks, sparsity, step, first_step=SUBBLOCK_FIRST_STEP):
+    return int(lib().oracle_subblock_keep(n_blocks, float(sparsity), step, first_step))
+
+
+def subblock_select(scores, keep):
+    """scores [heads, nbq, nbk] -> int32 [heads, nbq, keep] kept key blocks, ascending."""
+    scores = np.ascontiguousarray(scores, dtype=np.float64)
+    heads, nbq, nbk = scores.shape
+    assert 0 <= keep <= nbk
+    out = np.zeros((heads, nbq, keep), dtype=np.int32)
+    lib().oracle_subblock_select(_ptr(out), _ptr(scores), heads, nbq, nbk, keep)
+    return out
+
+
+def subblock_route(q, k, block, sparsity, step, first_step=SUBBLOCK_FIRST_STEP):
+    """Whole router: (kv_blocks int32 [heads, nb, keep], scores float64 [heads, nb, nb])."""
+    pq = subblock_pool(q, block)
+    pk = subblock_pool(k, block)
+    s = subblock_scores(pq, pk)
+    keep = subblock_keep(pk.shape[1], sparsity, step, first_step)
+    return subblock_select(s, keep), s

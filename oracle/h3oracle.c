@@ -12,6 +12,7 @@
 #include "h3oracle.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -313,4 +314,94 @@ void oracle_residual_l1(double* out, const void* cur, const void* prev,
     }
     out[0] = num;
     out[1] = den;
+}
+
+/* ---------------------------------------------------------------------------
+ * Block-sparse attention router.  The report page (section "Só com três
+ * camadas…", SubBlock paragraph) describes a block router that, from the
+ * tenth denoising step on, keeps only part of the key/value blocks (sparsity
+ * 0.75 or 0.80); the newsletter page says the skipped blocks are the ones
+ * that matter least.  Block size, pooling and score are not given.  Reading:
+ * mean-pool each block of tokens per head, score a (query block, key block)
+ * pair by the dot product of the two means -- which equals the average
+ * attention logit q.k over all token pairs of the two blocks -- and keep the
+ * highest-scoring key blocks.
+ * ------------------------------------------------------------------------- */
+void oracle_subblock_pool(double* pooled, const void* x, int dtype,
+                          int64_t rows, int32_t heads, int32_t head_dim,
+                          int32_t block) {
+    const int64_t nb = (rows + block - 1) / block;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t r0 = b * block;
+        const int64_t r1 = r0 + block < rows ? r0 + block : rows;
+        for (int32_t h = 0; h < heads; ++h) {
+            for (int32_t d = 0; d < head_dim; ++d) {
+                double s = 0.0;
+                for (int64_t r = r0; r < r1; ++r)
+                    s += ld(x, dtype, (r * heads + h) * head_dim + d);
+                pooled[((int64_t)h * nb + b) * head_dim + d] = s / (double)(r1 - r0);
+            }
+        }
+    }
+}
+
+void oracle_subblock_scores(double* scores, const double* pq, const double* pk,
+                            int32_t heads, int64_t nbq, int64_t nbk,
+                            int32_t head_dim) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nbq; ++i) {
+        for (int32_t h = 0; h < heads; ++h) {
+            const double* a = pq + ((int64_t)h * nbq + i) * head_dim;
+            for (int64_t j = 0; j < nbk; ++j) {
+                const double* c = pk + ((int64_t)h * nbk + j) * head_dim;
+                double s = 0.0;
+                for (int32_t d = 0; d < head_dim; ++d) s += a[d] * c[d];
+                scores[((int64_t)h * nbq + i) * nbk + j] = s;
+            }
+        }
+    }
+}
+
+int64_t oracle_subblock_keep(int64_t nb, double sparsity, int32_t step,
+                             int32_t first_step) {
+    if (step < first_step) return nb;
+    const double skipped = sparsity * (double)nb;
+    return nb - (int64_t)floor(skipped);
+}
+
+typedef struct {
+    double score;
+    int32_t block;
+} scored_block;
+
+/* larger score first; equal scores: lower block index first */
+static int by_score_desc(const void* pa, const void* pb) {
+    const scored_block* a = (const scored_block*)pa;
+    const scored_block* b = (const scored_block*)pb;
+    if (a->score > b->score) return -1;
+    if (a->score < b->score) return 1;
+    return (a->block > b->block) - (a->block < b->block);
+}
+
+static int by_index_asc(const void* pa, const void* pb) {
+    const int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+    return (a > b) - (a < b);
+}
+
+void oracle_subblock_select(int32_t* kv, const double* scores, int32_t heads,
+                            int64_t nbq, int64_t nbk, int64_t keep) {
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < (int64_t)heads * nbq; ++row) {
+        scored_block* tmp = (scored_block*)malloc((size_t)nbk * sizeof *tmp);
+        for (int64_t j = 0; j < nbk; ++j) {
+            tmp[j].score = scores[row * nbk + j];
+            tmp[j].block = (int32_t)j;
+        }
+        qsort(tmp, (size_t)nbk, sizeof *tmp, by_score_desc);
+        int32_t* out = kv + row * keep;
+        for (int64_t t = 0; t < keep; ++t) out[t] = tmp[t].block;
+        qsort(out, (size_t)keep, sizeof *out, by_index_asc);
+        free(tmp);
+    }
 }

@@ -139,6 +139,32 @@ void oracle_gated_residual_adaln(void* x, int x_dtype, const void* h,
 void oracle_residual_l1(double* out, const void* cur, const void* prev,
                         int dtype, int64_t rows, int64_t hidden);
 
+/* --- block-sparse attention router (SubBlock) ----------------------------------
+ * Token block b holds rows [b*block, min(rows, (b+1)*block)); the last block
+ * may be short.  x is [rows, heads, head_dim].
+ * pooled[h, b, d] = mean over the rows of block b of x[r, h, d] (double). */
+void oracle_subblock_pool(double* pooled, const void* x, int dtype,
+                          int64_t rows, int32_t heads, int32_t head_dim,
+                          int32_t block);
+
+/* scores[h, i, j] = sum_d pq[h, i, d] * pk[h, j, d]: the mean of q_a . k_b over
+ * every token pair (a in query block i, b in key block j).
+ * pq is [heads, nbq, head_dim], pk [heads, nbk, head_dim]. */
+void oracle_subblock_scores(double* scores, const double* pq, const double* pk,
+                            int32_t heads, int64_t nbq, int64_t nbk,
+                            int32_t head_dim);
+
+/* Key blocks kept per query block at denoising step `step` (1-based): all of
+ * them before step first_step, else nb - floor(sparsity * nb) (sparsity is the
+ * skipped fraction; the product is one double multiply). */
+int64_t oracle_subblock_keep(int64_t nb, double sparsity, int32_t step,
+                             int32_t first_step);
+
+/* kv[h, i, 0:keep] = the keep key blocks with the largest scores[h, i, :]
+ * (equal scores: lower block index first), listed in ascending block order. */
+void oracle_subblock_select(int32_t* kv, const double* scores, int32_t heads,
+                            int64_t nbq, int64_t nbk, int64_t keep);
+
 #ifdef __cplusplus
 }
 #endif

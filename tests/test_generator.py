@@ -14,6 +14,11 @@ def test_deterministic_and_row_addressable():
     assert np.array_equal(h3gen.host_rows("x", sel, 96, "f32", seed=0), a[sel])
 
 
+def test_column_window_matches_full_rows():
+    full = h3gen.host_rows("k", 40, 640, "bf16", seed=2)
+    assert np.array_equal(h3gen.host_cols("k", 40, 640, 384, 128, "bf16", seed=2), full[:, 384:512])
+
+
 def test_streams_differ_by_seed_and_tensor():
     a = h3gen.host_rows("x", 4, 64, "f32", seed=0)
     assert not np.array_equal(a, h3gen.host_rows("x", 4, 64, "f32", seed=1))

@@ -38,6 +38,19 @@ MUTANTS = {
     "audio_position_axis": ("t = (int32_t)(p - n_video);\n            h = 0;",
                             "t = 0;\n            h = (int32_t)(p - n_video);"),
     "bf16_round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u + 0 * lsb;"),
+    "subblock_sum_not_mean": ("= s / (double)(r1 - r0);", "= s;"),
+    "subblock_full_block_divisor": ("= s / (double)(r1 - r0);", "= s / (double)block;"),
+    "subblock_wrong_head": ("ld(x, dtype, (r * heads + h) * head_dim + d)",
+                            "ld(x, dtype, (r * heads + 0) * head_dim + d)"),
+    "subblock_scores_transposed": ("scores[((int64_t)h * nbq + i) * nbk + j] = s;",
+                                   "scores[((int64_t)h * nbq + j) * nbk + i] = s;"),
+    "subblock_keep_ceil": ("nb - (int64_t)floor(skipped)", "nb - (int64_t)ceil(skipped)"),
+    "subblock_keep_step_off_by_one": ("if (step < first_step) return nb;",
+                                      "if (step <= first_step) return nb;"),
+    "subblock_select_smallest": ("if (a->score > b->score) return -1;\n    if (a->score < b->score) return 1;",
+                                 "if (a->score > b->score) return 1;\n    if (a->score < b->score) return -1;"),
+    "subblock_ties_higher_index": ("return (a->block > b->block) - (a->block < b->block);",
+                                   "return (a->block < b->block) - (a->block > b->block);"),
 }
 
 

@@ -486,3 +486,108 @@ def test_residual_l1():
     cur = f32(RNG.standard_normal((5, 16)))
     num, _ = oracle.residual_l1(cur, prev)
     assert num == pytest.approx(np.abs(as_f64(cur) - as_f64(prev)).sum(), rel=1e-12)
+
+
+# ----------------------------------------------------------------------------------
+# block-sparse attention router (SubBlock)
+# ----------------------------------------------------------------------------------
+
+def pair_mean_logits(q, k, block):
+    """Average of q_a . k_b over every token pair (a in query block i, b in key
+    block j), by explicit pairs -- no pooling -- for each head."""
+    qf, kf = as_f64(q), as_f64(k)
+    rows, heads, _ = qf.shape
+    nb = (rows + block - 1) // block
+    out = np.zeros((heads, nb, nb))
+    for h in range(heads):
+        logits = qf[:, h, :] @ kf[:, h, :].T          # every token pair
+        for i in range(nb):
+            for j in range(nb):
+                out[h, i, j] = logits[i * block:(i + 1) * block, j * block:(j + 1) * block].mean()
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_subblock_score_is_mean_pair_logit(dtype):
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((37, 2, 8))
+    k = rng.standard_normal((37, 2, 8)) + 0.3
+    if dtype == "f32":
+        q, k = f32(q), f32(k)
+    else:
+        q, k = bf16_bits(q), bf16_bits(k)
+    pq = oracle.subblock_pool(q, 10)                   # blocks of 10, 10, 10, 7
+    pk = oracle.subblock_pool(k, 10)
+    assert pq.shape == (2, 4, 8)
+    s = oracle.subblock_scores(pq, pk)
+    ref = pair_mean_logits(q, k, 10)
+    assert np.abs(s - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def test_subblock_pool_of_constant_blocks():
+    # every token of block b holds the value b + 1 (short last block included)
+    x = np.zeros((23, 1, 4), np.float32)
+    for r in range(23):
+        x[r] = r // 8 + 1
+    p = oracle.subblock_pool(x, 8)
+    assert np.array_equal(p[0], np.repeat(np.array([[1.0], [2.0], [3.0]]), 4, axis=1))
+
+
+def test_subblock_keep_closed_form():
+    # nb - floor(sparsity * nb), from the tenth step on
+    assert oracle.subblock_keep(978, 0.80, 10) == 978 - 782        # 782.4 skipped
+    assert oracle.subblock_keep(978, 0.75, 10) == 978 - 733        # 733.5 skipped
+    assert oracle.subblock_keep(1924, 0.80, 50) == 1924 - 1539     # 1539.2 skipped
+    assert oracle.subblock_keep(1924, 0.75, 11) == 1924 - 1443     # 1443 exactly
+    assert oracle.subblock_keep(978, 0.80, 9) == 978               # dense before step 10
+    assert oracle.subblock_keep(978, 0.80, 1) == 978
+    assert oracle.subblock_keep(32, 0.0, 10) == 32
+
+
+def test_subblock_select_planted_ranking():
+    rng = np.random.default_rng(3)
+    nb = 40
+    s = np.stack([rng.permutation(nb).astype(np.float64) for _ in range(6)]).reshape(2, 3, nb)
+    kv = oracle.subblock_select(s, 7)
+    for h in range(2):
+        for i in range(3):
+            want = np.sort(np.nonzero(s[h, i] >= nb - 7)[0])   # the 7 largest values 33..39
+            assert np.array_equal(kv[h, i], want)
+
+
+def test_subblock_select_matches_torch_topk():
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal((3, 5, 97))
+    kv = oracle.subblock_select(s, 20)
+    top = torch.topk(torch.tensor(s), 20, dim=-1).indices.sort(dim=-1).values.numpy()
+    assert np.array_equal(kv, top.astype(np.int32))
+
+
+def test_subblock_select_ties_take_lower_index():
+    s = np.zeros((1, 2, 10))
+    s[0, 1, :] = [1, 5, 5, 0, 5, 5, 2, 5, 0, 0]
+    kv = oracle.subblock_select(s, 3)
+    assert kv[0, 0].tolist() == [0, 1, 2]                 # all equal: lowest indices
+    assert kv[0, 1].tolist() == [1, 2, 4]                 # five 5s tie for three places
+
+
+def test_subblock_route_planted_blocks():
+    # query tokens all e0; key block j tokens all alpha_j * e0, so the pair-mean
+    # logit of every (i, j) is alpha_j.  The short last block has the largest
+    # alpha: a sum (not mean) pooling or a full-block divisor would demote it.
+    block, rows = 16, 16 * 5 + 3
+    alpha = [0.25, 2.0, -1.0, 0.5, 1.0, 4.0]
+    q = np.zeros((rows, 2, 128), np.float32)
+    k = np.zeros((rows, 2, 128), np.float32)
+    q[:, :, 0] = 1.0
+    for r in range(rows):
+        k[r, 0, 0] = alpha[r // block]
+        k[r, 1, 0] = -alpha[r // block]                   # second head ranks in reverse
+    kv, s = oracle.subblock_route(bf16_bits(q), bf16_bits(k), block, 0.5, 10)
+    assert s.shape == (2, 6, 6) and kv.shape == (2, 6, 3)
+    assert np.array_equal(s[0], np.tile(alpha, (6, 1)))
+    for i in range(6):
+        assert kv[0, i].tolist() == [1, 4, 5]             # 2.0, 1.0, 4.0
+        assert kv[1, i].tolist() == [0, 2, 3]             # -0.25, 1.0, -0.5
+    kv_dense, _ = oracle.subblock_route(bf16_bits(q), bf16_bits(k), block, 0.5, 9)
+    assert kv_dense.shape == (2, 6, 6) and (kv_dense == np.arange(6)).all()
