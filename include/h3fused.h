@@ -68,7 +68,8 @@ typedef enum {
     H3F_ERR_ALIASING = 6,
     H3F_ERR_LAUNCH = 7,
     H3F_ERR_UNSUPPORTED = 8,
-    H3F_ERR_WORKSPACE = 9
+    H3F_ERR_WORKSPACE = 9,
+    H3F_ERR_BAD_VALUE = 10
 } h3f_status_t;
 
 /* RoPE pair layouts inside one axis chunk of size d_c */
@@ -225,6 +226,59 @@ h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cur_row_strid
                              const void* prev, int64_t prev_row_stride, h3f_dtype_t dtype,
                              int64_t rows, int64_t hidden, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse attention router (SubBlock).  The report page (section "Só com
+ * três camadas…", SubBlock paragraph) describes a block router that, from the
+ * tenth denoising step on, cuts the key/value blocks each attention
+ * computation uses, at sparsity 0.75 or 0.80; the newsletter page says the
+ * blocks skipped are the least important ones; the report page's section
+ * "Alguns limites…" restricts it to long non-causal attention in BF16 with
+ * head dimension 128 and at least 4096 tokens.  Block size, pooling and score
+ * are not given.  Reading implemented here, per head h:
+ *   - token block b = rows [b*block, min(rows, (b+1)*block)), the last one
+ *     possibly short; n_blocks = ceil(rows / block) for queries and keys;
+ *   - qm[h,b,:], km[h,b,:] = mean over the block's tokens (fp32);
+ *   - scores[h,i,j] = qm[h,i,:] . km[h,j,:], the mean attention logit q.k of
+ *     all token pairs of query block i and key block j (the softmax scale
+ *     1/sqrt(head_dim) is a positive constant and does not change the order);
+ *   - kv_blocks[h,i,0:keep] = the keep key blocks with the largest scores
+ *     (equal scores: lower block index first), in ascending block order;
+ *   - keep = n_blocks - floor(sparsity * n_blocks) (one double multiply; the
+ *     skipped fraction is sparsity) at step >= H3F_SUBBLOCK_FIRST_STEP, and
+ *     keep = n_blocks (every block, dense attention) before it.  Steps count
+ *     from 1.
+ *
+ * h3f_subblock_plan: host-only sizes of one call.  *n_blocks, *keep and
+ * *workspace_bytes (any may be NULL) receive the block count, the key blocks
+ * kept per query block, and the device scratch the route call needs.
+ *
+ * h3f_subblock_route: q, k are bf16 [rows, heads, head_dim] with their own
+ * row / head strides in elements (e.g. the q, k outputs of
+ * h3f_qk_rmsnorm_rope3d; strides multiples of 8, pointers 16-byte aligned).
+ * kv_blocks: device int32 [heads, n_blocks, keep], dense, 4-byte aligned.
+ * scores: device fp32 [heads, n_blocks, n_blocks], dense, 4-byte aligned,
+ * written on routed steps only.  workspace: device scratch of at least
+ * workspace_bytes (16-byte aligned, no initialisation needed; calls sharing
+ * one must be ordered on one stream).  Outputs and workspace must not overlap
+ * each other or q, k.  On a dense step (step < H3F_SUBBLOCK_FIRST_STEP) the
+ * call only writes kv_blocks[h,i,:] = 0..n_blocks-1 and reads neither q nor k.
+ * Errors: H3F_ERR_UNSUPPORTED for a dtype other than bf16, head_dim != 128,
+ * rows < 4096 or n_blocks > 8192; H3F_ERR_BAD_VALUE for sparsity outside
+ * [0, 1) or step < 1; H3F_ERR_BAD_SHAPE for block < 1 or heads < 1.
+ * Deterministic: fixed summation order; bit-identical run to run.
+ */
+#define H3F_SUBBLOCK_FIRST_STEP 10
+h3f_status_t h3f_subblock_plan(int64_t rows, int32_t heads, int32_t head_dim, int32_t block,
+                               double sparsity, int32_t step, int32_t* n_blocks, int32_t* keep,
+                               size_t* workspace_bytes);
+h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores,
+                                const void* q, int64_t q_row_stride, int64_t q_head_stride,
+                                const void* k, int64_t k_row_stride, int64_t k_head_stride,
+                                h3f_dtype_t dtype, int64_t rows, int32_t heads,
+                                int32_t head_dim, int32_t block, double sparsity,
+                                int32_t step, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /*
  * Streaming copy (measurement helper, not an operator): dst[0:bytes) =

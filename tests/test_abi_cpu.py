@@ -14,7 +14,7 @@ import video_diffusion_transformer_h3f_amd as h3
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "h3fused.h")
 
-OK, NULLP, SHAPE, STRIDE, MISAL, DTYPE, ALIAS, LAUNCH, UNSUP, WORKSPACE = range(10)
+OK, NULLP, SHAPE, STRIDE, MISAL, DTYPE, ALIAS, LAUNCH, UNSUP, WORKSPACE, BADVAL = range(11)
 F32, BF16 = 0, 1
 
 
@@ -41,8 +41,8 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_status_strings():
     L = h3.lib()
-    for s in range(10):
-        assert L.h3f_status_string(s)
+    for s in range(11):
+        assert L.h3f_status_string(s) != b"unknown status"
     assert L.h3f_status_string(99) == b"unknown status"
 
 
@@ -255,3 +255,71 @@ def test_residual_l1_validation():
     assert l1(ws=P(0x40000008)) == WORKSPACE
     assert l1(ws=A(1)) == ALIAS
     assert l1(out=A(2)) == ALIAS
+
+
+# --- block-sparse attention router ---------------------------------------------------------
+
+def test_subblock_plan_sizes():
+    # 5 s sequence: 125,120 tokens in blocks of 128 -> 978 blocks; sparsity 0.8 skips
+    # floor(782.4) = 782 of them from the tenth step on
+    assert h3.h3f_subblock_plan(125120, 40, 128, 128, 0.8, 10) == (978, 196, 2 * 40 * 978 * 128 * 4)
+    assert h3.h3f_subblock_plan(125120, 40, 128, 128, 0.75, 50)[1] == 978 - 733
+    assert h3.h3f_subblock_plan(125120, 40, 128, 128, 0.8, 9)[1] == 978
+    assert h3.h3f_subblock_plan(246208, 40, 128, 128, 0.8, 10)[:2] == (1924, 1924 - 1539)
+    # the largest sparsity below 1 still keeps one block
+    assert h3.h3f_subblock_plan(4096, 1, 128, 1024, 1.0 - 2.0 ** -53, 10)[1] == 1
+
+
+def test_subblock_plan_validation():
+    def plan(rows=8192, heads=8, hd=128, block=128, sp=0.8, step=10):
+        return L.h3f_subblock_plan(rows, heads, hd, block, sp, step, None, None, None)
+
+    assert plan() == OK
+    assert plan(rows=4095) == UNSUP            # sequence shorter than 4096 tokens
+    assert plan(hd=64) == UNSUP                # head dimension other than 128
+    assert plan(rows=8193 * 128, block=128) == UNSUP  # more than 8192 blocks
+    assert plan(block=0) == SHAPE
+    assert plan(heads=0) == SHAPE
+    assert plan(sp=1.0) == BADVAL
+    assert plan(sp=-0.01) == BADVAL
+    assert plan(sp=float("nan")) == BADVAL
+    assert plan(step=0) == BADVAL
+
+
+def test_subblock_route_validation():
+    # 4096 tokens x 8 heads x 128 (8 KB rows / 32 MB per tensor), 32 blocks of 128;
+    # fake device addresses 256 MB apart: every call below fails validation.
+    def route(kv=A(0), sc=A(1), q=A(2), qrs=1024, qhs=128, k=A(3), krs=1024, khs=128, dt=BF16,
+              rows=4096, heads=8, hd=128, block=128, sp=0.8, step=10, ws=A(4), wsb=1 << 20):
+        return L.h3f_subblock_route(kv, sc, q, qrs, qhs, k, krs, khs, dt, rows, heads, hd, block,
+                                    sp, step, ws, wsb, None)
+
+    assert route(kv=None) == NULLP
+    assert route(sc=None) == NULLP
+    assert route(k=None) == NULLP
+    assert route(dt=3) == DTYPE
+    assert route(dt=F32) == UNSUP              # the router runs on bf16 q / k only
+    assert route(rows=2048) == UNSUP
+    assert route(hd=64, qhs=64, khs=64) == UNSUP
+    assert route(sp=1.5) == BADVAL
+    assert route(q=P(0x30000008)) == MISAL
+    assert route(kv=P(0x10000002)) == MISAL
+    assert route(qrs=1020) == STRIDE
+    assert route(khs=120) == STRIDE
+    assert route(qrs=512) == STRIDE            # rows would overlap (8 heads x 128 > 512)
+    assert route(ws=None) == WORKSPACE
+    assert route(wsb=2 * 8 * 32 * 512 - 16) == WORKSPACE
+    assert route(ws=P(0x50000008)) == WORKSPACE
+    assert route(sc=A(2)) == ALIAS             # scores on top of q
+    assert route(ws=P(0x10000000 + 64)) == ALIAS   # workspace inside kv_blocks
+    assert route(kv=P(0x40000000 + 1024)) == ALIAS  # kv_blocks inside k
+
+
+def test_subblock_binding_checks_shapes_before_the_library():
+    import torch
+
+    q = torch.zeros(4096, 2, 128, dtype=torch.bfloat16)
+    kv = torch.zeros(2, 32, 7, dtype=torch.int32)
+    sc = torch.zeros(2, 32, 32)
+    with pytest.raises(ValueError):
+        h3.h3f_subblock_route(kv, sc, q, q, 128, 0.8, 10)

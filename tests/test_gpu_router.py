@@ -1,0 +1,193 @@
+"""GPU parity of the block-sparse attention router (h3f_subblock_route) against
+the CPU oracle.
+
+Block scores are fp32 outputs and meet the fp32 tolerance of every other
+fp32 output (|err| <= 1e-6 + 1e-5 |ref|) against the oracle's fp64 scores.
+The kept key blocks are an integer decision taken from floating point, where
+several answers can be right when two scores are within rounding of each
+other, so they are checked as follows:
+  - exact on their own input: each row keeps blocks whose GPU scores are all
+    >= every skipped block's GPU score, equal scores going to the lower index,
+    listed strictly ascending (this pins the selection kernel bit for bit);
+  - valid against the oracle: no skipped block's oracle score exceeds a kept
+    block's oracle score by more than the two scores' tolerances;
+  - where scores are exact by construction (planted inputs), identical to the
+    oracle's selection.
+"""
+import numpy as np
+import pytest
+import torch
+
+import h3gen
+import oracle
+from gpu_util import DEV, dev_tensor, to_np
+from tolerance import FP32_ATOL, FP32_RTOL, assert_close
+
+pytestmark = pytest.mark.gpu
+
+h3 = pytest.importorskip("video_diffusion_transformer_h3f_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    h3.lib()
+    h3gen.dev_lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def qk_tensors(rows, heads, packed=False, seed=0):
+    """bf16 q, k [rows, heads, 128] on the GPU (views of one packed qkv buffer
+    when packed) and the matching host arrays."""
+    cols = heads * 128
+    if packed:
+        buf = torch.full((rows, 3, heads, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+        q, k = buf[:, 0], buf[:, 1]
+        flat = buf.view(rows, 3 * cols)
+        h3gen.fill_device(flat[:, :cols], "q", seed=seed)
+        h3gen.fill_device(flat[:, cols:2 * cols], "k", seed=seed)
+    else:
+        q = dev_tensor("q", rows, cols, "bf16", seed=seed).view(rows, heads, 128)
+        k = dev_tensor("k", rows, cols, "bf16", seed=seed).view(rows, heads, 128)
+    qh = h3gen.host_rows("q", rows, cols, "bf16", seed=seed).reshape(rows, heads, 128)
+    kh = h3gen.host_rows("k", rows, cols, "bf16", seed=seed).reshape(rows, heads, 128)
+    return q, k, qh, kh
+
+
+def run_route(q, k, block, sparsity, step, sentinel=None):
+    rows, heads, _ = q.shape
+    nb, keep, _ = h3.h3f_subblock_plan(rows, heads, 128, block, sparsity, step)
+    kv = torch.full((heads, nb, keep), -7, dtype=torch.int32, device=DEV)
+    sc = torch.full((heads, nb, nb), float("nan") if sentinel is None else sentinel,
+                    dtype=torch.float32, device=DEV)
+    h3.h3f_subblock_route(kv, sc, q, k, block, sparsity, step)
+    torch.cuda.synchronize()
+    return to_np(kv), to_np(sc)
+
+
+def check_selection_on_own_scores(kv, sc):
+    """Every row of kv is the top-keep of its own row of sc (ties: lower index)."""
+    heads, nbq, keep = kv.shape
+    nbk = sc.shape[2]
+    assert kv.min() >= 0 and kv.max() < nbk
+    assert (np.diff(kv, axis=2) > 0).all(), "kept blocks must be strictly ascending"
+    kept = np.zeros(sc.shape, dtype=bool)
+    np.put_along_axis(kept, kv.astype(np.int64), True, axis=2)
+    if keep == nbk:
+        return
+    s = sc.astype(np.float64)
+    lo = np.where(kept, s, np.inf).min(axis=2)          # smallest kept score
+    hi = np.where(kept, -np.inf, s).max(axis=2)         # largest skipped score
+    assert (lo >= hi).all(), "a skipped block outscores a kept block"
+    # equal to the threshold and skipped: must come after every kept block of that score
+    thr = lo[..., None]
+    idx = np.arange(nbk)
+    last_kept_at_thr = np.where(kept & (s == thr), idx, -1).max(axis=2)
+    first_skipped_at_thr = np.where(~kept & (s == thr), idx, nbk).min(axis=2)
+    assert (first_skipped_at_thr > last_kept_at_thr).all(), "ties must go to the lower index"
+
+
+def check_selection_valid(kv, ref_scores):
+    """No skipped block's oracle score beats a kept block's by more than the tolerances."""
+    s = ref_scores
+    tol = FP32_ATOL + FP32_RTOL * np.abs(s)
+    kept = np.zeros(s.shape, dtype=bool)
+    np.put_along_axis(kept, kv.astype(np.int64), True, axis=-1)
+    if kept.all():
+        return
+    lo = np.where(kept, s + tol, np.inf).min(axis=-1)
+    hi = np.where(kept, -np.inf, s - tol).max(axis=-1)
+    assert (lo >= hi).all(), "selection inconsistent with the oracle's scores"
+
+
+@pytest.mark.parametrize("rows,heads,block,packed", [
+    (4096 + 77, 3, 128, False),   # ragged last block, a partial group of heads
+    (4096, 8, 64, True),          # strided q / k inside a packed qkv buffer
+    (5000, 2, 1000, False),       # long blocks, ragged
+    (4096 + 77, 1, 4096 + 77, False),  # a single block
+], ids=["ragged", "packed", "long-blocks", "one-block"])
+@pytest.mark.parametrize("sparsity", [0.8, 0.75])
+def test_router_matches_oracle(rows, heads, block, packed, sparsity):
+    print(f"router rows={rows} heads={heads} block={block} packed={packed} s={sparsity}", flush=True)
+    q, k, qh, kh = qk_tensors(rows, heads, packed=packed, seed=3)
+    kv, sc = run_route(q, k, block, sparsity, step=10)
+    kv_ref, sc_ref = oracle.subblock_route(qh, kh, block, sparsity, 10)
+    assert kv.shape == kv_ref.shape and sc.shape == sc_ref.shape
+    assert_close(sc, sc_ref, "f32", "block scores")
+    check_selection_on_own_scores(kv, sc)
+    check_selection_valid(kv, sc_ref)
+    agree = np.mean([len(np.intersect1d(a, b)) / kv.shape[2]
+                     for a, b in zip(kv.reshape(-1, kv.shape[2]), kv_ref.reshape(-1, kv.shape[2]))])
+    print(f"  kept sets agree with the oracle's on {agree:.4%} of entries")
+
+
+def test_router_planted_scores_exact():
+    # Every query token is e0; every token of key block j is alpha_j * e0 (head h
+    # uses (-1)^h alpha).  Block means and scores are exact in fp32, so the kept
+    # blocks must equal the oracle's exactly, ties included (alpha repeats).
+    rows, heads, block = 4096 + 40, 5, 128
+    nb = (rows + block - 1) // block
+    rng = np.random.default_rng(11)
+    alpha = rng.integers(-16, 17, size=nb).astype(np.float32) / 8.0   # many ties
+    q = np.zeros((rows, heads, 128), np.float32)
+    k = np.zeros((rows, heads, 128), np.float32)
+    q[:, :, 0] = 1.0
+    sign = np.array([(-1.0) ** h for h in range(heads)], np.float32)
+    k[:, :, 0] = alpha[np.arange(rows) // block][:, None] * sign[None, :]
+    qb = torch.from_numpy(q).to(torch.bfloat16).to(DEV)
+    kb = torch.from_numpy(k).to(torch.bfloat16).to(DEV)
+    qh = qb.cpu().view(torch.int16).numpy().view(np.uint16)
+    kh = kb.cpu().view(torch.int16).numpy().view(np.uint16)
+    for sparsity in (0.8, 0.5, 0.0):
+        kv, sc = run_route(qb, kb, block, sparsity, step=12)
+        kv_ref, sc_ref = oracle.subblock_route(qh, kh, block, sparsity, 12)
+        assert np.array_equal(sc.astype(np.float64), sc_ref)
+        assert np.array_equal(kv, kv_ref), f"sparsity {sparsity}"
+
+
+def test_router_dense_steps_keep_everything():
+    q, k, _, _ = qk_tensors(4096 + 5, 2, seed=1)
+    kv, sc = run_route(q, k, 128, 0.8, step=9, sentinel=123.0)
+    nb = 33
+    assert kv.shape == (2, nb, nb)
+    assert (kv == np.arange(nb, dtype=np.int32)).all()
+    assert (sc == 123.0).all(), "a dense step must not write scores"
+
+
+def test_router_sparsity_zero_keeps_all_in_order():
+    q, k, _, _ = qk_tensors(4096, 2, seed=2)
+    kv, sc = run_route(q, k, 256, 0.0, step=10)
+    assert (kv == np.arange(16, dtype=np.int32)).all()
+    assert np.isfinite(sc).all()
+
+
+def test_router_deterministic():
+    q, k, _, _ = qk_tensors(8192 + 100, 4, seed=4)
+    a = run_route(q, k, 128, 0.8, step=20)
+    b = run_route(q, k, 128, 0.8, step=20)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_router_full_5s_sampled():
+    # The 5 s sequence (125,120 tokens, 40 heads of 128, blocks of 128 -> 978
+    # blocks, sparsity 0.8 -> 196 kept), launched as the benchmark launches it.
+    # The oracle recomputes every block mean of sampled heads and the score rows
+    # of sampled query blocks (the first, a middle and the short last one); the
+    # selection property is checked on every row.
+    rows, heads, block = 31 * 48 * 84 + 128, 40, 128
+    q, k, _, _ = (dev_tensor("q", rows, heads * 128, "bf16").view(rows, heads, 128),
+                  dev_tensor("k", rows, heads * 128, "bf16").view(rows, heads, 128), None, None)
+    kv, sc = run_route(q, k, block, 0.8, step=10)
+    assert kv.shape == (40, 978, 196)
+    check_selection_on_own_scores(kv, sc)
+    qblocks = np.array([0, 1, 500, 977])
+    for h in (0, 17, 39):
+        qh = h3gen.host_cols("q", rows, heads * 128, h * 128, 128).reshape(rows, 1, 128)
+        kh = h3gen.host_cols("k", rows, heads * 128, h * 128, 128).reshape(rows, 1, 128)
+        pq = oracle.subblock_pool(qh, block)[:, qblocks]
+        pk = oracle.subblock_pool(kh, block)
+        ref = oracle.subblock_scores(pq, pk)[0]
+        assert_close(sc[h, qblocks], ref, "f32", f"scores head {h}")
+        check_selection_valid(kv[h, qblocks], ref)

@@ -24,13 +24,16 @@ H3F_ROPE_HALF_SPLIT = 1
 STATUS = {
     0: "H3F_OK", 1: "H3F_ERR_NULL_POINTER", 2: "H3F_ERR_BAD_SHAPE", 3: "H3F_ERR_BAD_STRIDE",
     4: "H3F_ERR_MISALIGNED", 5: "H3F_ERR_BAD_DTYPE", 6: "H3F_ERR_ALIASING", 7: "H3F_ERR_LAUNCH",
-    8: "H3F_ERR_UNSUPPORTED", 9: "H3F_ERR_WORKSPACE",
+    8: "H3F_ERR_UNSUPPORTED", 9: "H3F_ERR_WORKSPACE", 10: "H3F_ERR_BAD_VALUE",
 }
+
+H3F_SUBBLOCK_FIRST_STEP = 10
 
 EXPORTS = [
     "h3f_abi_version", "h3f_status_string", "h3f_rope3d_positions", "h3f_adaln_modulate",
     "h3f_gated_residual", "h3f_swiglu", "h3f_qk_rmsnorm_rope3d", "h3f_gated_residual_adaln",
     "h3f_stream_copy", "h3f_residual_l1_workspace_bytes", "h3f_residual_l1",
+    "h3f_subblock_plan", "h3f_subblock_route",
 ]
 
 
@@ -82,6 +85,11 @@ def lib():
             getattr(L, name).restype = st
         L.h3f_residual_l1_workspace_bytes.argtypes = [i64, i64, st]
         L.h3f_residual_l1_workspace_bytes.restype = ctypes.c_size_t
+        L.h3f_subblock_plan.argtypes = [i64, i32, i32, i32, ctypes.c_double, i32,
+                                        ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                        ctypes.POINTER(ctypes.c_size_t)]
+        L.h3f_subblock_route.argtypes = [p, p, p, i64, i64, p, i64, i64, st, i64, i32, i32, i32,
+                                         ctypes.c_double, i32, p, ctypes.c_size_t, p]
         _lib = L
     return _lib
 
@@ -323,6 +331,46 @@ def h3f_residual_l1(out, cur, prev, workspace=None, stream=None):
         _ptr(out), _ptr(cur), cs, _ptr(prev), ps, _dtype(cur), rows, hidden, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(dev, stream)))
     return out
+
+
+def h3f_subblock_plan(rows: int, heads: int, head_dim: int, block: int, sparsity: float,
+                      step: int):
+    """(n_blocks, keep, workspace_bytes) of one router call (host-only)."""
+    nb, keep, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
+    _check("h3f_subblock_plan", lib().h3f_subblock_plan(
+        rows, heads, head_dim, block, float(sparsity), step, ctypes.byref(nb), ctypes.byref(keep),
+        ctypes.byref(ws)))
+    return nb.value, keep.value, ws.value
+
+
+def h3f_subblock_route(kv_blocks, scores, q, k, block: int, sparsity: float, step: int,
+                       workspace=None, stream=None):
+    """Block-sparse attention router.  q, k: bf16 [rows, heads, head_dim] views;
+    kv_blocks: int32 [heads, n_blocks, keep]; scores: float32 [heads, n_blocks,
+    n_blocks] (both contiguous; sizes from h3f_subblock_plan).  workspace: uint8
+    GPU tensor of at least the planned bytes; allocated here (torch) when None."""
+    import torch
+
+    dev = _dev(kv_blocks, scores, q, k)
+    shp, qrs, qhs = _heads3d(q, "q")
+    kshp, krs, khs = _heads3d(k, "k")
+    if shp != kshp:
+        raise ValueError("q and k shapes differ")
+    rows, heads, head_dim = shp
+    if kv_blocks.dtype != torch.int32 or scores.dtype != torch.float32:
+        raise TypeError("kv_blocks must be int32 and scores float32")
+    if not (kv_blocks.is_contiguous() and scores.is_contiguous()):
+        raise ValueError("kv_blocks and scores must be contiguous")
+    nb, keep, need = h3f_subblock_plan(rows, heads, head_dim, block, sparsity, step)
+    if tuple(kv_blocks.shape) != (heads, nb, keep) or tuple(scores.shape) != (heads, nb, nb):
+        raise ValueError(f"kv_blocks must be [{heads}, {nb}, {keep}] and scores [{heads}, {nb}, {nb}]")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check("h3f_subblock_route", lib().h3f_subblock_route(
+        _ptr(kv_blocks), _ptr(scores), _ptr(q), qrs, qhs, _ptr(k), krs, khs, _dtype(q), rows,
+        heads, head_dim, block, float(sparsity), step, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev, stream)))
+    return kv_blocks, scores
 
 
 def h3f_stream_copy(dst, src, stream=None):

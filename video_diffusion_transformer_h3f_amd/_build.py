@@ -13,7 +13,7 @@ LIB = os.path.join(PKG, "libh3fused.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "k_elementwise.hip", "k_adaln.hip", "k_qk_rope.hip", "k_reduce.hip"]
+SOURCES = ["api.hip", "k_elementwise.hip", "k_adaln.hip", "k_qk_rope.hip", "k_reduce.hip", "k_router.hip"]
 
 # Packed-fp32 VALU forms are disabled: hipcc -O3 would otherwise emit them from
 # plain float code.

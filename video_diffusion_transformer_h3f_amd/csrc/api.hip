@@ -15,6 +15,7 @@ extern "C" const char* h3f_status_string(h3f_status_t status) {
         case H3F_ERR_LAUNCH: return "kernel launch failed";
         case H3F_ERR_UNSUPPORTED: return "size or layout outside the supported range";
         case H3F_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case H3F_ERR_BAD_VALUE: return "argument value outside its valid range";
     }
     return "unknown status";
 }
