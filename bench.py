@@ -71,6 +71,13 @@ def op_bytes(name, N, c, x_bytes=2):
     raise KeyError(name)
 
 
+def router_bytes(N, c, nb, keep):
+    """Algorithmic bytes of one router call: q and k read once (bf16), the fp32
+    block scores and the int32 kept-block lists written once."""
+    H, Dh = c["heads"], c["Dh"]
+    return 2 * N * H * Dh * 2 + H * nb * nb * 4 + H * nb * keep * 4
+
+
 def source_digest(names):
     h = hashlib.sha256()
     for n in names:
@@ -292,6 +299,31 @@ def main():
                                     "GBps": round(b / (avg * 1e-3) / 1e9, 1),
                                     "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
         del x_prev, ws
+
+        # Block-sparse attention router on the step's post-RoPE q / k (what attention
+        # reads), blocks of 128 tokens, sparsity 0.8, a routed step.
+        blk, sp = 128, 0.8
+        nb, keep, need = h3.h3f_subblock_plan(N, c["heads"], c["Dh"], blk, sp, 10)
+        kv = torch.empty(c["heads"], nb, keep, dtype=torch.int32, device=dev)
+        sc = torch.empty(c["heads"], nb, nb, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            h3.h3f_subblock_route(kv, sc, t["q_out"], t["k_out"], blk, sp, 10, ws)
+        torch.cuda.synchronize()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record()
+        for _ in range(K):
+            h3.h3f_subblock_route(kv, sc, t["q_out"], t["k_out"], blk, sp, 10, ws)
+        r1.record()
+        torch.cuda.synchronize()
+        avg = r0.elapsed_time(r1) / K
+        b = router_bytes(N, c, nb, keep)
+        extra_ops["subblock_route"] = {
+            "avg_ms": round(avg, 4), "bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "block": blk, "sparsity": sp, "n_blocks": nb, "keep": keep,
+            "score_flops": 2 * c["heads"] * nb * nb * c["Dh"]}
+        del kv, sc, ws
 
     dom = "swiglu"
     roofline = {"bound": "hbm", "achieved": per_op[dom]["GBps"], "peak": PEAK_HBM_GBPS,

@@ -70,3 +70,21 @@ def qk_blocks(rows, heads, lph):
                                             (50, 3, 8), (40, 5, 32), (30, 2, 8), (9, 1, 64)])
 def test_qk_block_mapping_covers_each_slot_once(rows, heads, lph):
     qk_blocks(rows, heads, lph)
+
+
+def xcd_linear(w, n, xcds=8):
+    """The router score kernel's workgroup -> tile order: workgroup w runs on
+    XCD w mod 8; each XCD gets one contiguous run of tiles."""
+    per, extra = n // xcds, n % xcds
+    x, slot = w % xcds, w // xcds
+    return x * (per + 1) + slot if x < extra else extra * (per + 1) + (x - extra) * per + slot
+
+
+@pytest.mark.parametrize("n", [1, 3, 7, 8, 9, 17, 255, 256, 257, 40 * 16 * 16, 40 * 31 * 31])
+def test_xcd_tile_order_is_a_permutation(n):
+    tiles = [xcd_linear(w, n) for w in range(n)]
+    assert sorted(tiles) == list(range(n))
+    # each XCD's tiles form one contiguous run
+    for x in range(8):
+        mine = sorted(xcd_linear(w, n) for w in range(x, n, 8))
+        assert mine == list(range(mine[0], mine[0] + len(mine))) if mine else True

@@ -13,14 +13,14 @@
 //           order through LDS.
 //   score   scores[h] = Qm[h] Km[h]^T on the matrix cores: fp32 MFMA
 //           16x16x4, a 64x64 output tile per workgroup, 32x32 per wave.  The
-//           contraction index is split as d = 32 g + kk (g = lane / 16 picks
-//           the MFMA k slot, kk the instruction), so each lane reads 32
-//           consecutive floats of its row of Qm and of Km.
-//   select  one workgroup per (head, query block): the row of scores becomes
-//           order-preserving uint32 keys in LDS, a 4-pass 8-bit radix select
-//           finds the keep-th largest key T, and two ordered prefix sums emit
-//           every block with key > T plus the lowest-index blocks with key ==
-//           T, in ascending block order.
+//           contraction index is split as d = 16 v + 4 g + e (g = lane / 16
+//           picks the MFMA k slot, instruction 4 v + e), the same split for
+//           both operands, so the 4 lanes of a row read 64 contiguous bytes.
+//   select  one wavefront per (head, query block): the row of scores becomes
+//           order-preserving uint32 keys in registers, the keep-th largest
+//           key T is found bit by bit with ballot counts, and ballot
+//           compaction emits every block with key > T plus the lowest-index
+//           blocks with key == T, in ascending block order.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -44,6 +44,9 @@ constexpr int kMaxBlocks = 8192;
 #endif
 #ifndef H3F_POOL_UNROLL
 #define H3F_POOL_UNROLL 8
+#endif
+#ifndef H3F_POOL_ROWWG
+#define H3F_POOL_ROWWG 0
 #endif
 constexpr int kPoolWaves = H3F_POOL_WAVES;
 constexpr int kPoolUnroll = H3F_POOL_UNROLL;
@@ -129,6 +132,62 @@ __global__ void __launch_bounds__(64 * WAVES) subblock_pool_kernel(PoolArgs a) {
     reinterpret_cast<float4*>(dst)[1] = m1;
 }
 
+// Whole-row form: one workgroup per (tensor, block, chunk of up to 64 heads)
+// with one wavefront per 4 heads; every wavefront walks all rows of the block,
+// so the workgroup streams the block's rows front to back.
+constexpr int kRowWaves = 16;
+
+template <int U>
+__global__ void __launch_bounds__(64 * kRowWaves) subblock_pool_rows_kernel(PoolArgs a) {
+    const uint32_t n_chunks = (a.n_groups + kRowWaves - 1) / kRowWaves;
+    const uint32_t per_tensor = a.n_blocks * n_chunks;
+    const uint32_t t = blockIdx.x >= per_tensor ? 1u : 0u;
+    const uint32_t rem = blockIdx.x - t * per_tensor;
+    const uint32_t b = rem / n_chunks;
+    const uint32_t z = rem - b * n_chunks;
+    const int lane = threadIdx.x & 63;
+    const uint32_t grp = z * kRowWaves + (threadIdx.x >> 6);
+    if (grp >= a.n_groups) return;  // whole wavefront; no barrier in this kernel
+    const int head = (int)grp * kHeadsPerGroup + (lane >> 4);
+    const int c = lane & 15;
+
+    const int64_t r0 = (int64_t)b * a.block;
+    const int64_t nrows = std::min<int64_t>(a.block, a.rows - r0);
+    const int64_t rs = a.row_stride[t];
+    const int64_t hs = a.head_stride[t];
+    const int64_t row_span = (int64_t)(a.heads - 1) * hs + kHeadDim * 2;
+    const rsrc_t rsrc = make_rsrc(a.base[t] + r0 * rs, span_bytes(nrows, rs, row_span));
+    const uint32_t col = (uint32_t)(std::min(head, a.heads - 1) * hs) + (uint32_t)c * 16u;
+
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    const int n = (int)nrows;
+    for (int r = 0; r < n; r += U) {
+        Vec<__bf16, 8> v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u].template load_buf<kLoadStream>(rsrc, (uint32_t)(r + u) * (uint32_t)rs + col);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (r + u < n) {
+                float f[8];
+                v[u].to_float(f);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += f[i];
+            }
+        }
+    }
+    if (head >= a.heads) return;
+    const float fn = (float)nrows;
+    float4 m0, m1;
+    m0.x = acc[0] / fn; m0.y = acc[1] / fn; m0.z = acc[2] / fn; m0.w = acc[3] / fn;
+    m1.x = acc[4] / fn; m1.y = acc[5] / fn; m1.z = acc[6] / fn; m1.w = acc[7] / fn;
+    float* dst = a.pooled + (((size_t)t * a.heads + head) * a.n_blocks + b) * kHeadDim + c * 8;
+    reinterpret_cast<float4*>(dst)[0] = m0;
+    reinterpret_cast<float4*>(dst)[1] = m1;
+}
+
 // ---------------------------------------------------------------------------
 // score (fp32 MFMA)
 // ---------------------------------------------------------------------------
@@ -145,11 +204,13 @@ struct ScoreArgs {
     uint32_t tiles;       // ceil(nb / 64)
 };
 
-// 32 consecutive floats of row `row` starting at column 32 * g, zero past nb.
+// The 32 floats of row `row` this lane feeds to the MFMAs: columns
+// 16 v + 4 g + e (v < 8, e < 4) in register 4 v + e, zero past nb.  Per load
+// instruction the 4 lanes of a row read one contiguous 64-byte piece of it.
 __device__ __forceinline__ void load_row32(float (&dst)[32], rsrc_t r, uint32_t row, int g) {
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-        const u32x4 x = buf_ld<kLoadReuse>(r, row * (kHeadDim * 4u) + (uint32_t)g * 128u + 16u * v);
+        const u32x4 x = buf_ld<kLoadReuse>(r, row * (kHeadDim * 4u) + 64u * v + (uint32_t)g * 16u);
         dst[4 * v + 0] = __uint_as_float(x[0]);
         dst[4 * v + 1] = __uint_as_float(x[1]);
         dst[4 * v + 2] = __uint_as_float(x[2]);
@@ -157,10 +218,22 @@ __device__ __forceinline__ void load_row32(float (&dst)[32], rsrc_t r, uint32_t 
     }
 }
 
+// Workgroups are dealt to the 8 XCDs round robin (workgroup w runs on XCD
+// w mod 8).  Tile t = xcd_base + w / 8 gives each XCD one contiguous run of
+// tiles, so the few heads in flight on an XCD share its L2.
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_linear(uint32_t w, uint32_t n) {
+    const uint32_t per = n / kXcds, extra = n % kXcds;
+    const uint32_t x = w % kXcds, slot = w / kXcds;
+    return x < extra ? x * (per + 1) + slot : extra * (per + 1) + (x - extra) * per + slot;
+}
+
 __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
     const uint32_t per_head = a.tiles * a.tiles;
-    const uint32_t h = blockIdx.x / per_head;
-    const uint32_t rem = blockIdx.x - h * per_head;
+    const uint32_t tile = xcd_linear(blockIdx.x, (uint32_t)a.heads * per_head);
+    const uint32_t h = tile / per_head;
+    const uint32_t rem = tile - h * per_head;
     const uint32_t ti = rem / a.tiles;
     const uint32_t tj = rem - ti * a.tiles;
     const int lane = threadIdx.x & 63;
@@ -212,120 +285,281 @@ __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
     }
 }
 
+// Strip form: a workgroup keeps one 64-row tile of Qm in registers and walks
+// a run of kScoreRun 64-column tiles of Km, loading the next tile's operands
+// while the matrix cores work on the current one (two register sets,
+// alternating; the run is fully unrolled so the loads in flight are tracked
+// exactly).  The MFMA is fed Km as its first operand and Qm as its second, so
+// it produces the transposed tile: lane (ri, g) holds scores[i0 + ri][j0 +
+// 4 g .. 4 g + 3], one 16-byte store per 16 x 16 tile.  Column tiles past the
+// last one read zeros and store nothing.
+#ifndef H3F_SCORE_STRIP
+#define H3F_SCORE_STRIP 1
+#endif
+#ifndef H3F_SCORE_RUN
+#define H3F_SCORE_RUN 8
+#endif
+constexpr uint32_t kScoreRun = H3F_SCORE_RUN;  // column tiles per workgroup
+
+__device__ __forceinline__ void mfma_tile32_t(f32x4 (&acc)[2][2], const float (&A)[2][32],
+                                              const float (&B)[2][32]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(B[n][kk], A[m][kk], acc[m][n], 0, 0, 0);
+    }
+}
+
+// acc[m][n][e] = scores[i0 + 16 m + ri][j0 + 16 n + 4 g + e].  Stores go
+// through a buffer resource over the head's score matrix; an element outside
+// the matrix gets an offset past the resource's end and is dropped, so there
+// is no branch.  Rows start 16-byte aligned when nb % 4 == 0 (one 16-byte
+// store), 8-byte aligned when nb is even (two 8-byte stores), else 4 stores.
+constexpr uint32_t kDropped = 0xFFFFFFF0u;
+
+__device__ __forceinline__ void store_tile32_t(rsrc_t r, uint32_t nb, uint32_t i0, uint32_t j0,
+                                               int ri, int g, const f32x4 (&acc)[2][2]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const uint32_t i = i0 + 16 * m + ri;
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const uint32_t j = j0 + 16 * n + 4 * g;
+            const uint32_t off = (i * nb + j) * 4u;
+            const f32x4 v = acc[m][n];
+            if ((nb & 3u) == 0) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r,
+                                                       i < nb && j < nb ? off : kDropped, 0, 0);
+            } else if ((nb & 1u) == 0) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const u32x2 w = {__float_as_uint(v[2 * p]), __float_as_uint(v[2 * p + 1])};
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        w, r, i < nb && j + 2 * p < nb ? off + 8u * p : kDropped, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __float_as_uint(v[e]), r, i < nb && j + e < nb ? off + 4u * e : kDropped, 0, 0);
+            }
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) subblock_score_strip_kernel(ScoreArgs a) {
+    const uint32_t runs = (a.tiles + kScoreRun - 1) / kScoreRun;
+    const uint32_t per_head = a.tiles * runs;
+    const uint32_t w = xcd_linear(blockIdx.x, (uint32_t)a.heads * per_head);
+    const uint32_t h = w / per_head;
+    const uint32_t rem = w - h * per_head;
+    const uint32_t ti = rem / runs;
+    const uint32_t run = rem - ti * runs;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int ri = lane & 15;
+    const int g = lane >> 4;
+    const uint32_t i0 = ti * kTile + (wave >> 1) * kWaveTile;
+    const uint32_t jbase = run * kScoreRun * kTile + (wave & 1) * kWaveTile;
+
+    const uint32_t mat_bytes = a.nb * kHeadDim * 4u;
+    const rsrc_t rq = make_rsrc(a.pooled + (size_t)h * a.nb * kHeadDim, mat_bytes);
+    const rsrc_t rk = make_rsrc(a.pooled + ((size_t)a.heads + h) * a.nb * kHeadDim, mat_bytes);
+    const rsrc_t ro = make_rsrc(a.scores + (size_t)h * a.nb * a.nb, a.nb * a.nb * 4u);
+
+    float A[2][32], B[2][2][32];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) load_row32(A[m], rq, i0 + 16 * m + ri, g);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) load_row32(B[0][n], rk, jbase + 16 * n + ri, g);
+    f32x4 acc[2][2];
+#pragma unroll
+    for (uint32_t t = 0; t < kScoreRun; ++t) {
+        if (t + 1 < kScoreRun) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                load_row32(B[(t + 1) & 1][n], rk, jbase + (t + 1) * kTile + 16 * n + ri, g);
+        }
+        // keep the next tile's loads ahead of this tile's matrix instructions
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_tile32_t(acc, A, B[t & 1]);
+        store_tile32_t(ro, a.nb, i0, jbase + t * kTile, ri, g, acc);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // select
 // ---------------------------------------------------------------------------
-constexpr int kSelThreads = 256;
+constexpr int kSelWaves = 4;  // rows per workgroup, one wavefront each
 
 struct SelectArgs {
     const float* scores;  // [heads][nb][nb]
     int32_t* kv;          // [heads][nb][keep]
+    uint32_t rows;        // heads * nb
     uint32_t nb;
     uint32_t keep;
 };
 
-// Order-preserving map of a finite float to uint32 (-0 is taken as +0).
+// Order-preserving map of a float to uint32 (-0 is taken as +0).
 __device__ __forceinline__ uint32_t order_key(float s) {
     uint32_t u = __float_as_uint(s);
     if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of v over the workgroup in thread order; *total gets
-// the sum.  Uses red[0..4].
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* red, uint32_t* total) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) red[wave] = x;
-    __syncthreads();
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-        const uint32_t s = red[w];
-        if (w < wave) before += s;
-        all += s;
-    }
-    __syncthreads();  // red may be reused by the next scan
-    *total = all;
-    return before + x - v;
+// The float an order key stands for.
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
 }
 
-__global__ void __launch_bounds__(kSelThreads) subblock_select_kernel(SelectArgs a) {
-    extern __shared__ uint32_t keys[];
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t red[4];
-    __shared__ uint32_t found_digit, found_above;
-    const uint32_t row = blockIdx.x;  // h * nb + i
-    const float* s = a.scores + (size_t)row * a.nb;
-    for (uint32_t j = threadIdx.x; j < a.nb; j += kSelThreads) keys[j] = order_key(s[j]);
-
-    // Radix select of the keep-th largest key, 8 bits at a time from the top.
-    uint32_t prefix = 0, mask = 0, need = a.keep;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[threadIdx.x] = 0;
-        __syncthreads();
-        for (uint32_t j = threadIdx.x; j < a.nb; j += kSelThreads) {
-            const uint32_t key = keys[j];
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (threadIdx.x < 64) {
-            const int L = threadIdx.x;
-            const uint32_t c0 = hist[4 * L], c1 = hist[4 * L + 1], c2 = hist[4 * L + 2],
-                           c3 = hist[4 * L + 3];
-            const uint32_t own = c0 + c1 + c2 + c3;
-            uint32_t x = own;  // inclusive sum over lanes >= L
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t y = __shfl_down(x, off, 64);
-                if (L + off < 64) x += y;
-            }
-            // ge[d]: keys (matching the prefix) whose digit is >= d
-            const uint32_t ge3 = x - own + c3, ge2 = ge3 + c2, ge1 = ge2 + c1, ge0 = ge1 + c0;
-            const uint32_t above = x - own;  // digits > 4L + 3
-            // the digit is the largest d with ge[d] >= need; exactly one lane owns it
-            if (ge3 >= need && above < need) { found_digit = 4 * L + 3; found_above = above; }
-            else if (ge2 >= need && ge3 < need) { found_digit = 4 * L + 2; found_above = ge3; }
-            else if (ge1 >= need && ge2 < need) { found_digit = 4 * L + 1; found_above = ge2; }
-            else if (ge0 >= need && ge1 < need) { found_digit = 4 * L; found_above = ge1; }
-        }
-        __syncthreads();
-        prefix |= found_digit << shift;
-        mask |= 255u << shift;
-        need -= found_above;
-        __syncthreads();  // found_* are rewritten by the next pass
-    }
-    const uint32_t T = prefix;  // the keep-th largest key; `need` keys equal to it are kept
+    for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
 
-    // Each thread owns a contiguous run of block indices, so thread-order
-    // prefix sums are block-order prefix sums.
-    const uint32_t per = (a.nb + kSelThreads - 1) / kSelThreads;
-    const uint32_t j0 = std::min(a.nb, threadIdx.x * per);
-    const uint32_t j1 = std::min(a.nb, j0 + per);
-    uint32_t n_eq = 0;
-    for (uint32_t j = j0; j < j1; ++j) n_eq += keys[j] == T ? 1u : 0u;
-    uint32_t total;
-    const uint32_t eq_before = block_exclusive_scan(n_eq, red, &total);
-    uint32_t n_sel = 0;
-    for (uint32_t j = j0, e = eq_before; j < j1; ++j) {
-        const uint32_t key = keys[j];
-        if (key > T) ++n_sel;
-        else if (key == T) { n_sel += e < need ? 1u : 0u; ++e; }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
+// Number of lanes below this one whose bit is set in mask.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// One wavefront per row of scores; lane L holds keys of blocks L + 64 m,
+// m < KPL (nb <= 64 KPL).  The keep-th largest key T is bracketed by a search
+// over [min key, max key] with the invariant count(key >= lo) >= keep >
+// count(key > hi); each count is a ballot per register and a scalar popcount.
+// Probes interpolate linearly between the bracket's float values and counts,
+// falling back to the value midpoint when a step does not halve the keys in
+// the bracket, and to the integer midpoint when neither splits it.  The search
+// stops at a probe with exactly keep keys at or above it, or once at most 64
+// keys remain in the bracket; those are sorted across the lanes and T is read
+// at its rank.  The kept blocks -- every key > T, then keys == T in block
+// order until keep are taken -- are written in block order by ballot
+// compaction.  LDS holds only each wave's own 64 candidates; no barrier.
+template <int KPL>
+__global__ void __launch_bounds__(64 * kSelWaves) subblock_select_kernel(SelectArgs a) {
+    // wave-uniform (readfirstlane), so the row's buffer resource lives in SGPRs
+    const uint32_t row = __builtin_amdgcn_readfirstlane(blockIdx.x * kSelWaves + (threadIdx.x >> 6));
+    if (row >= a.rows) return;  // whole wavefront
+    const uint32_t lane = threadIdx.x & 63;
+    // All KPL loads are issued before any is used: a buffer resource over the
+    // row returns 0 past its end, so no load sits behind a branch.
+    const rsrc_t rs = make_rsrc(a.scores + (size_t)row * a.nb, a.nb * 4u);
+    uint32_t sv[KPL];  // raw fp32 bits
+#pragma unroll
+    for (int m = 0; m < KPL; ++m)
+        sv[m] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rs, (lane + 64u * m) * 4u, 0, kLoadStream));
+    uint32_t key[KPL];
+    // Padding slots hold key 0 and real keys are >= 1, so every probe (> lo >=
+    // 1) and the final threshold leave the padding out without a separate test.
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const bool valid = lane + 64u * m < a.nb;
+        const uint32_t k = max(order_key(__uint_as_float(sv[m])), 1u);
+        key[m] = valid ? k : 0u;
+        kmin = min(kmin, valid ? k : 0xFFFFFFFFu);
+        kmax = max(kmax, key[m]);
     }
-    const uint32_t sel_before = block_exclusive_scan(n_sel, red, &total);
+    auto count_ge = [&](uint32_t t) {
+        uint32_t n = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) n += (uint32_t)__popcll(__ballot(key[m] >= t));
+        return n;
+    };
+    // Invariant: count(key >= lo) = c_lo >= keep > c_hi = count(key > hi).
+    uint32_t lo = __builtin_amdgcn_readfirstlane(wave_min_u32(kmin));
+    uint32_t hi = __builtin_amdgcn_readfirstlane(wave_max_u32(kmax));
+    uint32_t c_lo = a.nb, c_hi = 0;
+    bool interpolate = true, exact = false;
+    for (int probe = 0; lo < hi && c_lo - c_hi > 64u; ++probe) {
+        const float vlo = key_value(lo), vhi = key_value(hi);
+        // interpolation: where a straight line through (vlo, c_lo), (vhi, c_hi)
+        // crosses keep; bisection of the value interval when the last
+        // interpolation step did not halve the candidates
+        const float f = interpolate ? ((float)(c_lo - a.keep) + 0.5f) *
+                                          __builtin_amdgcn_rcpf((float)(c_lo - c_hi))
+                                    : 0.5f;
+        uint32_t mid = order_key(vlo + f * (vhi - vlo));
+        if (probe >= 24 || !(mid > lo && mid <= hi)) mid = lo + ((hi - lo) >> 1) + 1u;
+        const uint32_t c = count_ge(mid);
+        const uint32_t before = c_lo - c_hi;
+        if (c >= a.keep) {
+            lo = mid;
+            c_lo = c;
+            if (c == a.keep) {
+                exact = true;
+                break;
+            }
+        } else {
+            hi = mid - 1u;
+            c_hi = c;
+        }
+        interpolate = !interpolate || 2u * (c_lo - c_hi) <= before;
+    }
+    uint32_t T, n_gt;
+    if (!exact && lo < hi) {
+        // At most 64 keys lie in [lo, hi]: gather them into one register per
+        // lane (wave-private LDS, in block order), sort them descending with a
+        // 64-lane bitonic network, and read T at rank keep - c_hi.
+        __shared__ uint32_t cand[kSelWaves][64];
+        uint32_t* my = cand[threadIdx.x >> 6];
+        uint32_t n = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) {
+            const bool in = key[m] >= lo && key[m] <= hi;
+            const uint64_t mask = __ballot(in);
+            const uint32_t at = n + lanes_below(mask);
+            if (in && at < 64u) my[at] = key[m];
+            n += (uint32_t)__popcll(mask);
+        }
+        __builtin_amdgcn_wave_barrier();
+        uint32_t v = lane < n ? my[lane] : 0u;  // 0 sorts below every key
+#pragma unroll
+        for (uint32_t k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+            for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+                const uint32_t other = (uint32_t)__shfl_xor((int)v, (int)j, 64);
+                const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
+                v = keep_max ? max(v, other) : min(v, other);
+            }
+        }
+        T = __builtin_amdgcn_readlane(v, (int)(a.keep - c_hi - 1u));
+        n_gt = c_hi + (uint32_t)__popcll(__ballot(v > T));
+    } else {
+        T = lo;
+        n_gt = T == 0xFFFFFFFFu ? 0u : count_ge(T + 1u);
+    }
+    const uint32_t need = a.keep - n_gt;  // keys equal to T to take, lowest blocks first
+
     int32_t* out = a.kv + (size_t)row * a.keep;
-    uint32_t pos = sel_before;
-    for (uint32_t j = j0, e = eq_before; j < j1; ++j) {
-        const uint32_t key = keys[j];
-        bool take = key > T;
-        if (key == T) { take = e < need; ++e; }
-        if (take && pos < a.keep) out[pos++] = (int32_t)j;  // exactly keep are taken
+    uint32_t pos = 0, eq_seen = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const uint32_t j = lane + 64u * m;
+        const bool gt = key[m] > T;
+        const bool eq = key[m] == T;  // T >= 1: padding never matches
+        const uint64_t eq_mask = __ballot(eq);
+        const bool take = gt || (eq && eq_seen + lanes_below(eq_mask) < need);
+        const uint64_t take_mask = __ballot(take);
+        const uint32_t at = pos + lanes_below(take_mask);
+        if (take && at < a.keep) out[at] = (int32_t)j;  // exactly keep are taken
+        pos += (uint32_t)__popcll(take_mask);
+        eq_seen += (uint32_t)__popcll(eq_mask);
     }
 }
 
@@ -404,7 +638,7 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
     if (!rows_separate(rq) || !rows_separate(rk)) return H3F_ERR_BAD_STRIDE;
     // one block of rows (plus the rows an unrolled batch reads past its end,
     // which must stay outside the resource) is addressed with 32-bit offsets
-    if ((int64_t)(block + kPoolUnroll * kPoolWaves) * std::max(q_row_stride, k_row_stride) * 2 +
+    if ((int64_t)(block + (kPoolUnroll + 1) * kPoolWaves) * std::max(q_row_stride, k_row_stride) * 2 +
             2 * std::max(q_span, k_span) > 0xFFFFFFF0ll)
         return H3F_ERR_UNSUPPORTED;
 
@@ -444,8 +678,17 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
     pa.n_blocks = (uint32_t)nb;
     pa.n_groups = (uint32_t)((heads + kHeadsPerGroup - 1) / kHeadsPerGroup);
     pa.pooled = static_cast<float*>(workspace);
+#if H3F_POOL_ROWWG
+    {
+        const uint32_t n_chunks = (pa.n_groups + kRowWaves - 1) / kRowWaves;
+        const uint32_t waves = std::min<uint32_t>(pa.n_groups, kRowWaves);
+        hipLaunchKernelGGL((subblock_pool_rows_kernel<kPoolUnroll>),
+                           dim3(2 * pa.n_blocks * n_chunks), dim3(64 * waves), 0, s, pa);
+    }
+#else
     hipLaunchKernelGGL((subblock_pool_kernel<kPoolWaves, kPoolUnroll>),
                        dim3(2 * pa.n_blocks * pa.n_groups), dim3(64 * kPoolWaves), 0, s, pa);
+#endif
 
     ScoreArgs sa;
     sa.pooled = pa.pooled;
@@ -453,15 +696,29 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
     sa.heads = heads;
     sa.nb = (uint32_t)nb;
     sa.tiles = (uint32_t)((nb + kTile - 1) / kTile);
+#if H3F_SCORE_STRIP
+    hipLaunchKernelGGL(subblock_score_strip_kernel,
+                       dim3((unsigned)(heads * sa.tiles * ((sa.tiles + kScoreRun - 1) / kScoreRun))),
+                       dim3(256), 0, s, sa);
+#else
     hipLaunchKernelGGL(subblock_score_kernel, dim3((unsigned)(heads * sa.tiles * sa.tiles)),
                        dim3(256), 0, s, sa);
+#endif
 
     SelectArgs se;
     se.scores = scores;
     se.kv = kv_blocks;
+    se.rows = (uint32_t)(heads * nb);
     se.nb = (uint32_t)nb;
     se.keep = (uint32_t)keep;
-    hipLaunchKernelGGL(subblock_select_kernel, dim3((unsigned)(heads * nb)), dim3(kSelThreads),
-                       (size_t)nb * sizeof(uint32_t), s, se);
+    const dim3 sg((se.rows + kSelWaves - 1) / kSelWaves), sb(64 * kSelWaves);
+    if (nb <= 64 * 4)
+        hipLaunchKernelGGL(subblock_select_kernel<4>, sg, sb, 0, s, se);
+    else if (nb <= 64 * 16)
+        hipLaunchKernelGGL(subblock_select_kernel<16>, sg, sb, 0, s, se);
+    else if (nb <= 64 * 32)
+        hipLaunchKernelGGL(subblock_select_kernel<32>, sg, sb, 0, s, se);
+    else
+        hipLaunchKernelGGL(subblock_select_kernel<128>, sg, sb, 0, s, se);
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }
