@@ -1,7 +1,8 @@
 /*
  * h3fused.h -- C ABI of libh3fused: fused, memory-bound per-token operators of
- * a single-stream audio+video diffusion transformer (MiniMax-H3 style DiT),
- * implemented as hand-written HIP kernels for gfx950 (MI355X, CDNA4).
+ * a single-stream audio+video diffusion transformer (MiniMax-H3 style DiT), and
+ * the block router of its block-sparse attention, implemented as hand-written
+ * HIP kernels for gfx950 (MI355X, CDNA4).
  *
  * Sources.  The operators are the ones the LMSYS performance report on
  * MiniMax-H3 with SGLang Diffusion names as fused kernels (summary page on

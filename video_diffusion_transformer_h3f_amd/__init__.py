@@ -1,5 +1,6 @@
 """Python binding of libh3fused (see include/h3fused.h): fused, memory-bound
-per-token DiT operators as hand-written HIP kernels for gfx950 (MI355X).
+per-token DiT operators and the block-sparse attention router, as hand-written
+HIP kernels for gfx950 (MI355X).
 
 Argument marshalling only.  Each function takes torch tensors that live on the
 GPU (torch provides device memory and the current stream), passes their

@@ -11,16 +11,18 @@
 //           when heads are packed -- and sums in fp32 in row order; the waves
 //           of a workgroup split the rows round-robin and are added in wave
 //           order through LDS.
-//   score   scores[h] = Qm[h] Km[h]^T on the matrix cores: fp32 MFMA
-//           16x16x4, a 64x64 output tile per workgroup, 32x32 per wave.  The
-//           contraction index is split as d = 16 v + 4 g + e (g = lane / 16
-//           picks the MFMA k slot, instruction 4 v + e), the same split for
-//           both operands, so the 4 lanes of a row read 64 contiguous bytes.
+//   score   scores[h] = Qm[h] Km[h]^T on the matrix cores (fp32 MFMA 16x16x4).
+//           A workgroup holds a 64-row tile of Qm in registers (32 x 32 per
+//           wave) and walks a run of 64-column tiles of Km with the next
+//           tile's loads in flight; the contraction index is split as
+//           d = 16 v + 4 g + e (g = lane / 16 picks the MFMA k slot,
+//           instruction 4 v + e), the same split for both operands, so the 4
+//           lanes of a row read 64 contiguous bytes.
 //   select  one wavefront per (head, query block): the row of scores becomes
-//           order-preserving uint32 keys in registers, the keep-th largest
-//           key T is found bit by bit with ballot counts, and ballot
-//           compaction emits every block with key > T plus the lowest-index
-//           blocks with key == T, in ascending block order.
+//           order-preserving uint32 keys in registers; an interpolation /
+//           bisection search with ballot counts brackets the keep-th largest
+//           key, a 64-lane sort of the last few candidates pins it down, and
+//           ballot compaction writes the kept blocks in ascending order.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -44,9 +46,6 @@ constexpr int kMaxBlocks = 8192;
 #endif
 #ifndef H3F_POOL_UNROLL
 #define H3F_POOL_UNROLL 8
-#endif
-#ifndef H3F_POOL_ROWWG
-#define H3F_POOL_ROWWG 0
 #endif
 constexpr int kPoolWaves = H3F_POOL_WAVES;
 constexpr int kPoolUnroll = H3F_POOL_UNROLL;
@@ -132,62 +131,6 @@ __global__ void __launch_bounds__(64 * WAVES) subblock_pool_kernel(PoolArgs a) {
     reinterpret_cast<float4*>(dst)[1] = m1;
 }
 
-// Whole-row form: one workgroup per (tensor, block, chunk of up to 64 heads)
-// with one wavefront per 4 heads; every wavefront walks all rows of the block,
-// so the workgroup streams the block's rows front to back.
-constexpr int kRowWaves = 16;
-
-template <int U>
-__global__ void __launch_bounds__(64 * kRowWaves) subblock_pool_rows_kernel(PoolArgs a) {
-    const uint32_t n_chunks = (a.n_groups + kRowWaves - 1) / kRowWaves;
-    const uint32_t per_tensor = a.n_blocks * n_chunks;
-    const uint32_t t = blockIdx.x >= per_tensor ? 1u : 0u;
-    const uint32_t rem = blockIdx.x - t * per_tensor;
-    const uint32_t b = rem / n_chunks;
-    const uint32_t z = rem - b * n_chunks;
-    const int lane = threadIdx.x & 63;
-    const uint32_t grp = z * kRowWaves + (threadIdx.x >> 6);
-    if (grp >= a.n_groups) return;  // whole wavefront; no barrier in this kernel
-    const int head = (int)grp * kHeadsPerGroup + (lane >> 4);
-    const int c = lane & 15;
-
-    const int64_t r0 = (int64_t)b * a.block;
-    const int64_t nrows = std::min<int64_t>(a.block, a.rows - r0);
-    const int64_t rs = a.row_stride[t];
-    const int64_t hs = a.head_stride[t];
-    const int64_t row_span = (int64_t)(a.heads - 1) * hs + kHeadDim * 2;
-    const rsrc_t rsrc = make_rsrc(a.base[t] + r0 * rs, span_bytes(nrows, rs, row_span));
-    const uint32_t col = (uint32_t)(std::min(head, a.heads - 1) * hs) + (uint32_t)c * 16u;
-
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    const int n = (int)nrows;
-    for (int r = 0; r < n; r += U) {
-        Vec<__bf16, 8> v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            v[u].template load_buf<kLoadStream>(rsrc, (uint32_t)(r + u) * (uint32_t)rs + col);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (r + u < n) {
-                float f[8];
-                v[u].to_float(f);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += f[i];
-            }
-        }
-    }
-    if (head >= a.heads) return;
-    const float fn = (float)nrows;
-    float4 m0, m1;
-    m0.x = acc[0] / fn; m0.y = acc[1] / fn; m0.z = acc[2] / fn; m0.w = acc[3] / fn;
-    m1.x = acc[4] / fn; m1.y = acc[5] / fn; m1.z = acc[6] / fn; m1.w = acc[7] / fn;
-    float* dst = a.pooled + (((size_t)t * a.heads + head) * a.n_blocks + b) * kHeadDim + c * 8;
-    reinterpret_cast<float4*>(dst)[0] = m0;
-    reinterpret_cast<float4*>(dst)[1] = m1;
-}
-
 // ---------------------------------------------------------------------------
 // score (fp32 MFMA)
 // ---------------------------------------------------------------------------
@@ -229,62 +172,6 @@ __device__ __forceinline__ uint32_t xcd_linear(uint32_t w, uint32_t n) {
     return x < extra ? x * (per + 1) + slot : extra * (per + 1) + (x - extra) * per + slot;
 }
 
-__global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
-    const uint32_t per_head = a.tiles * a.tiles;
-    const uint32_t tile = xcd_linear(blockIdx.x, (uint32_t)a.heads * per_head);
-    const uint32_t h = tile / per_head;
-    const uint32_t rem = tile - h * per_head;
-    const uint32_t ti = rem / a.tiles;
-    const uint32_t tj = rem - ti * a.tiles;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int ri = lane & 15;  // row of a 16-row operand tile this lane supplies
-    const int g = lane >> 4;   // MFMA k slot
-    const uint32_t i0 = ti * kTile + (wave >> 1) * kWaveTile;
-    const uint32_t j0 = tj * kTile + (wave & 1) * kWaveTile;
-
-    const uint32_t mat_bytes = a.nb * kHeadDim * 4u;
-    const float* qm = a.pooled + (size_t)h * a.nb * kHeadDim;
-    const float* km = a.pooled + ((size_t)a.heads + h) * a.nb * kHeadDim;
-    const rsrc_t rq = make_rsrc(qm, mat_bytes);
-    const rsrc_t rk = make_rsrc(km, mat_bytes);
-
-    float A[2][32], B[2][32];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) load_row32(A[m], rq, i0 + 16 * m + ri, g);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) load_row32(B[n], rk, j0 + 16 * n + ri, g);
-
-    f32x4 acc[2][2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 32; ++kk) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[m][kk], B[n][kk], acc[m][n], 0, 0, 0);
-    }
-    // Result element (row 4 * g + e, column ri) of each 16 x 16 tile sits in
-    // lane (ri, g), register e.
-    float* out = a.scores + (size_t)h * a.nb * a.nb;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const uint32_t j = j0 + 16 * n + ri;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t i = i0 + 16 * m + 4 * g + e;
-                if (i < a.nb && j < a.nb) out[(size_t)i * a.nb + j] = acc[m][n][e];
-            }
-        }
-    }
-}
-
 // Strip form: a workgroup keeps one 64-row tile of Qm in registers and walks
 // a run of kScoreRun 64-column tiles of Km, loading the next tile's operands
 // while the matrix cores work on the current one (two register sets,
@@ -293,9 +180,6 @@ __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
 // it produces the transposed tile: lane (ri, g) holds scores[i0 + ri][j0 +
 // 4 g .. 4 g + 3], one 16-byte store per 16 x 16 tile.  Column tiles past the
 // last one read zeros and store nothing.
-#ifndef H3F_SCORE_STRIP
-#define H3F_SCORE_STRIP 1
-#endif
 #ifndef H3F_SCORE_RUN
 #define H3F_SCORE_RUN 8
 #endif
@@ -354,7 +238,7 @@ __device__ __forceinline__ void store_tile32_t(rsrc_t r, uint32_t nb, uint32_t i
     }
 }
 
-__global__ void __launch_bounds__(256) subblock_score_strip_kernel(ScoreArgs a) {
+__global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
     const uint32_t runs = (a.tiles + kScoreRun - 1) / kScoreRun;
     const uint32_t per_head = a.tiles * runs;
     const uint32_t w = xcd_linear(blockIdx.x, (uint32_t)a.heads * per_head);
@@ -511,7 +395,7 @@ __global__ void __launch_bounds__(64 * kSelWaves) subblock_select_kernel(SelectA
         }
         interpolate = !interpolate || 2u * (c_lo - c_hi) <= before;
     }
-    uint32_t T, n_gt;
+    uint32_t T, n_gt, n_ge;
     if (!exact && lo < hi) {
         // At most 64 keys lie in [lo, hi]: gather them into one register per
         // lane (wave-private LDS, in block order), sort them descending with a
@@ -540,14 +424,28 @@ __global__ void __launch_bounds__(64 * kSelWaves) subblock_select_kernel(SelectA
         }
         T = __builtin_amdgcn_readlane(v, (int)(a.keep - c_hi - 1u));
         n_gt = c_hi + (uint32_t)__popcll(__ballot(v > T));
+        n_ge = n_gt + (uint32_t)__popcll(__ballot(v == T));
     } else {
-        T = lo;
+        T = lo;  // c_lo = count(key >= T)
         n_gt = T == 0xFFFFFFFFu ? 0u : count_ge(T + 1u);
+        n_ge = c_lo;
     }
     const uint32_t need = a.keep - n_gt;  // keys equal to T to take, lowest blocks first
 
     int32_t* out = a.kv + (size_t)row * a.keep;
     uint32_t pos = 0, eq_seen = 0;
+    if (n_ge == a.keep) {
+        // every key equal to T is kept: the kept blocks are exactly key >= T
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) {
+            const bool take = key[m] >= T;  // T >= 1: padding never matches
+            const uint64_t take_mask = __ballot(take);
+            const uint32_t at = pos + lanes_below(take_mask);
+            if (take && at < a.keep) out[at] = (int32_t)(lane + 64u * m);
+            pos += (uint32_t)__popcll(take_mask);
+        }
+        return;
+    }
 #pragma unroll
     for (int m = 0; m < KPL; ++m) {
         const uint32_t j = lane + 64u * m;
@@ -678,17 +576,8 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
     pa.n_blocks = (uint32_t)nb;
     pa.n_groups = (uint32_t)((heads + kHeadsPerGroup - 1) / kHeadsPerGroup);
     pa.pooled = static_cast<float*>(workspace);
-#if H3F_POOL_ROWWG
-    {
-        const uint32_t n_chunks = (pa.n_groups + kRowWaves - 1) / kRowWaves;
-        const uint32_t waves = std::min<uint32_t>(pa.n_groups, kRowWaves);
-        hipLaunchKernelGGL((subblock_pool_rows_kernel<kPoolUnroll>),
-                           dim3(2 * pa.n_blocks * n_chunks), dim3(64 * waves), 0, s, pa);
-    }
-#else
     hipLaunchKernelGGL((subblock_pool_kernel<kPoolWaves, kPoolUnroll>),
                        dim3(2 * pa.n_blocks * pa.n_groups), dim3(64 * kPoolWaves), 0, s, pa);
-#endif
 
     ScoreArgs sa;
     sa.pooled = pa.pooled;
@@ -696,14 +585,9 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
     sa.heads = heads;
     sa.nb = (uint32_t)nb;
     sa.tiles = (uint32_t)((nb + kTile - 1) / kTile);
-#if H3F_SCORE_STRIP
-    hipLaunchKernelGGL(subblock_score_strip_kernel,
+    hipLaunchKernelGGL(subblock_score_kernel,
                        dim3((unsigned)(heads * sa.tiles * ((sa.tiles + kScoreRun - 1) / kScoreRun))),
                        dim3(256), 0, s, sa);
-#else
-    hipLaunchKernelGGL(subblock_score_kernel, dim3((unsigned)(heads * sa.tiles * sa.tiles)),
-                       dim3(256), 0, s, sa);
-#endif
 
     SelectArgs se;
     se.scores = scores;
