@@ -258,15 +258,17 @@ h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cur_row_strid
  * row / head strides in elements (e.g. the q, k outputs of
  * h3f_qk_rmsnorm_rope3d; strides multiples of 8, pointers 16-byte aligned).
  * kv_blocks: device int32 [heads, n_blocks, keep], dense, 4-byte aligned.
- * scores: device fp32 [heads, n_blocks, n_blocks], dense, 4-byte aligned,
- * written on routed steps only.  workspace: device scratch of at least
+ * scores: device fp32 [heads, n_blocks, n_blocks], dense, 16-byte aligned,
+ * written on routed steps only (required on every step).  workspace: device scratch of at least
  * workspace_bytes (16-byte aligned, no initialisation needed; calls sharing
  * one must be ordered on one stream).  Outputs and workspace must not overlap
  * each other or q, k.  On a dense step (step < H3F_SUBBLOCK_FIRST_STEP) the
  * call only writes kv_blocks[h,i,:] = 0..n_blocks-1 and reads neither q nor k.
  * Errors: H3F_ERR_UNSUPPORTED for a dtype other than bf16, head_dim != 128,
- * rows < 4096 or n_blocks > 8192; H3F_ERR_BAD_VALUE for sparsity outside
- * [0, 1) or step < 1; H3F_ERR_BAD_SHAPE for block < 1 or heads < 1.
+ * rows < 4096 (unlike the per-token operators, rows == 0 is not a no-op),
+ * n_blocks > 8192, heads > 4096 or a stride above 2^31 elements;
+ * H3F_ERR_BAD_VALUE for sparsity outside [0, 1) or step < 1;
+ * H3F_ERR_BAD_SHAPE for block < 1 or heads < 1.
  * Deterministic: fixed summation order; bit-identical run to run.
  */
 #define H3F_SUBBLOCK_FIRST_STEP 10

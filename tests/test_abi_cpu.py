@@ -304,6 +304,8 @@ def test_subblock_route_validation():
     assert route(sp=1.5) == BADVAL
     assert route(q=P(0x30000008)) == MISAL
     assert route(kv=P(0x10000002)) == MISAL
+    assert route(sc=P(0x20000004)) == MISAL          # scores take 16-byte stores
+    assert route(qrs=(1 << 31) + 8) == UNSUP
     assert route(qrs=1020) == STRIDE
     assert route(khs=120) == STRIDE
     assert route(qrs=512) == STRIDE            # rows would overlap (8 heads x 128 > 512)
@@ -323,3 +325,19 @@ def test_subblock_binding_checks_shapes_before_the_library():
     sc = torch.zeros(2, 32, 32)
     with pytest.raises(ValueError):
         h3.h3f_subblock_route(kv, sc, q, q, 128, 0.8, 10)
+
+
+def test_absurd_strides_are_rejected_without_overflow():
+    # strides whose footprints exceed 2^62 bytes: refused before any span arithmetic
+    # could overflow (every value is a vector multiple, so only the size check can fire)
+    big = 1 << 61
+    assert gated(xs=big) == UNSUP
+    assert gated(rpg=5, gs=big) == UNSUP
+    assert swiglu(as_=big) == UNSUP
+    assert adaln(xs=big) == UNSUP
+    assert adaln(rpg=1, gs=big) == UNSUP
+    assert fused(hs=big) == UNSUP
+    assert qk(qhs=big) == UNSUP
+    assert qk(krs=big) == UNSUP
+    assert L.h3f_residual_l1(A(0), A(1), big, A(2), 512, BF16, 4, 512, A(3), 1 << 20,
+                             None) == UNSUP

@@ -237,3 +237,20 @@ def test_router_full_5s_sampled():
         # plain fp32 output tolerance
         assert_scores(sc[h, qblocks], ref, tol, f"scores head {h}", plain_fp32=True)
         check_selection_valid(kv[h, qblocks], ref, tol)
+
+
+def test_router_maximum_blocks():
+    # 8192 blocks, the largest call the select kernel takes (128 keys per lane, every
+    # slot filled); one-token blocks, one head
+    rows, heads, block = 8192, 1, 1
+    q, k, qh, kh = qk_tensors(rows, heads, seed=5)
+    kv, sc = run_route(q, k, block, 0.75, step=30)
+    assert kv.shape == (1, 8192, 8192 - 6144)
+    check_selection_on_own_scores(kv, sc)
+    kv_ref, sc_ref = oracle.subblock_route(qh, kh, block, 0.75, 30)
+    tol = score_tol(sc_ref, block_abs_means(qh, block), block_abs_means(kh, block), block)
+    assert_scores(sc, sc_ref, tol, "block scores at 8192 blocks")
+    check_selection_valid(kv, sc_ref, tol)
+    # one block more is refused before any launch
+    with pytest.raises(h3.H3FError):
+        h3.h3f_subblock_plan(8193, 1, 128, 1, 0.75, 30)

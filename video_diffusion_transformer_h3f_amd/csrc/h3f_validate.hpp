@@ -30,6 +30,16 @@ struct Region {
     uintptr_t hi() const { return base + (uintptr_t)((rows > 1 ? (rows - 1) * stride : 0) + span); }
 };
 
+// The byte extent of rows x cols elements, rows `stride` elements apart, is
+// below 2^62, so every footprint computed from these values (region2d, spans,
+// offsets) stays inside int64.  Evaluated in 128-bit arithmetic.
+inline bool extent_ok(int64_t rows, int64_t stride_elems, int64_t cols, int esize) {
+    if (rows <= 0 || cols <= 0) return true;
+    const __int128 s = stride_elems < 0 ? -(__int128)stride_elems : (__int128)stride_elems;
+    const __int128 ext = ((__int128)(rows - 1) * s + cols) * esize;
+    return ext < ((__int128)1 << 62);
+}
+
 inline Region region2d(const void* p, int64_t rows, int64_t row_stride_elems, int64_t cols,
                        int esize) {
     Region r;

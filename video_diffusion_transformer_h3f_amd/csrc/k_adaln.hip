@@ -243,6 +243,9 @@ extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t
     if ((s = check_mod(scale, groups, mod_group_stride, hidden, V)) != H3F_OK) return s;
     if (rows > 1 && (x_row_stride % V || y_row_stride % V)) return H3F_ERR_BAD_STRIDE;
     const int ex = dtype_bytes(x_dtype), ey = dtype_bytes(y_dtype);
+    if (!extent_ok(rows, x_row_stride, hidden, ex) || !extent_ok(rows, y_row_stride, hidden, ey) ||
+        !extent_ok(groups, mod_group_stride, hidden, ex))
+        return H3F_ERR_UNSUPPORTED;
     const Region rx = region2d(x, rows, x_row_stride, hidden, ex);
     const Region ry = region2d(y, rows, y_row_stride, hidden, ey);
     const Region rsh = region2d(shift, groups, mod_group_stride, hidden, ex);
@@ -299,6 +302,9 @@ extern "C" h3f_status_t h3f_gated_residual_adaln(
     if (rows > 1 && (x_row_stride % V || h_row_stride % V || y_row_stride % V))
         return H3F_ERR_BAD_STRIDE;
     const int ex = dtype_bytes(x_dtype), eh = dtype_bytes(h_dtype), ey = dtype_bytes(y_dtype);
+    if (!extent_ok(rows, x_row_stride, hidden, ex) || !extent_ok(rows, h_row_stride, hidden, eh) ||
+        !extent_ok(rows, y_row_stride, hidden, ey) || !extent_ok(groups, mod_group_stride, hidden, ex))
+        return H3F_ERR_UNSUPPORTED;
     const Region rx = region2d(x, rows, x_row_stride, hidden, ex);
     const Region rh = region2d(h, rows, h_row_stride, hidden, eh);
     const Region ry = region2d(y, rows, y_row_stride, hidden, ey);

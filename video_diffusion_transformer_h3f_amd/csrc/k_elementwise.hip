@@ -172,7 +172,9 @@ inline int64_t rows_per_launch(int64_t chunks_per_row) {
 // In-tile byte offsets are 32-bit: a tile covers at most this many rows.
 inline bool tile_fits(int64_t chunks_per_row, int64_t stride_bytes, int64_t row_bytes) {
     const int64_t tile_rows = kTile / chunks_per_row + 2;
-    return tile_rows * stride_bytes + row_bytes < 0xFFFFFFF0ll;
+    // tile_rows * stride_bytes + row_bytes < 0xFFFFFFF0, without overflow
+    if (row_bytes >= 0xFFFFFFF0ll) return false;
+    return stride_bytes <= (0xFFFFFFF0ll - row_bytes - 1) / tile_rows;
 }
 
 inline Stream stream_of(const void* base, int64_t stride_elems, int64_t rows, int64_t cols,
@@ -257,6 +259,9 @@ extern "C" h3f_status_t h3f_gated_residual(void* x, h3f_dtype_t x_dtype, int64_t
         (groups > 1 && gate_group_stride % V))
         return H3F_ERR_BAD_STRIDE;
     const int ex = dtype_bytes(x_dtype), eh = dtype_bytes(h_dtype);
+    if (!extent_ok(rows, x_row_stride, hidden, ex) || !extent_ok(rows, h_row_stride, hidden, eh) ||
+        !extent_ok(groups, gate_group_stride, hidden, ex))
+        return H3F_ERR_UNSUPPORTED;
     const Region rx = region2d(x, rows, x_row_stride, hidden, ex);
     const Region rh = region2d(h, rows, h_row_stride, hidden, eh);
     const Region rg = region2d(gate, groups, gate_group_stride, hidden, ex);
@@ -290,6 +295,9 @@ extern "C" h3f_status_t h3f_swiglu(void* out, int64_t out_row_stride, const void
     if (rows > 1 && (out_row_stride % V || a_row_stride % V || b_row_stride % V))
         return H3F_ERR_BAD_STRIDE;
     const int e = dtype_bytes(dtype);
+    if (!extent_ok(rows, out_row_stride, inner, e) || !extent_ok(rows, a_row_stride, inner, e) ||
+        !extent_ok(rows, b_row_stride, inner, e))
+        return H3F_ERR_UNSUPPORTED;
     const Region ro = region2d(out, rows, out_row_stride, inner, e);
     const Region ra = region2d(a, rows, a_row_stride, inner, e);
     const Region rb = region2d(b, rows, b_row_stride, inner, e);

@@ -318,6 +318,15 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
                       q_head_stride < head_dim || k_head_stride < head_dim))
         return H3F_ERR_BAD_STRIDE;
     const int e = dtype_bytes(dtype);
+    {
+        const int64_t rs_[] = {q_out_row_stride, k_out_row_stride, q_row_stride, k_row_stride};
+        const int64_t hs_[] = {q_out_head_stride, k_out_head_stride, q_head_stride, k_head_stride};
+        for (int i = 0; i < 4; ++i) {
+            if (!extent_ok(heads, hs_[i], head_dim, e)) return H3F_ERR_UNSUPPORTED;
+            const int64_t span = (heads > 1 ? (int64_t)(heads - 1) * hs_[i] : 0) + head_dim;
+            if (!extent_ok(rows, rs_[i], span, e)) return H3F_ERR_UNSUPPORTED;
+        }
+    }
     auto region = [&](const void* p, int64_t rs, int64_t hs) {
         const int64_t span = ((heads > 1 ? (int64_t)(heads - 1) * hs : 0) + head_dim);
         return region2d(p, rows, rows > 1 ? rs : span, span, e);
@@ -335,7 +344,8 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
             (heads > 1 ? e * std::max(std::max(q_out_head_stride, k_out_head_stride),
                                       std::max(q_head_stride, k_head_stride)) : 0);
         const int64_t span_max = std::max(std::max(rqo.span, rko.span), std::max(rq.span, rk.span));
-        if (span_max + 64 * hs_max > 0xFFFFFFF0ll) return H3F_ERR_UNSUPPORTED;
+        if (span_max > 0xFFFFFFF0ll || hs_max > (0xFFFFFFF0ll - span_max) / 64)
+            return H3F_ERR_UNSUPPORTED;
     }
     const Region rw1 = region2d(q_weight, 1, head_dim, head_dim, e);
     const Region rw2 = region2d(k_weight, 1, head_dim, head_dim, e);

@@ -142,7 +142,9 @@ inline int64_t n_partials(int64_t rows, int64_t cpr) {
 }
 
 inline bool tile_fits2(int64_t cpr, int64_t stride_bytes, int64_t row_bytes) {
-    return (kTile / cpr + 2) * stride_bytes + row_bytes < 0xFFFFFFF0ll;
+    // (kTile / cpr + 2) * stride_bytes + row_bytes < 0xFFFFFFF0, without overflow
+    if (row_bytes >= 0xFFFFFFF0ll) return false;
+    return stride_bytes <= (0xFFFFFFF0ll - row_bytes - 1) / (kTile / cpr + 2);
 }
 
 template <typename T, int VEC>
@@ -198,6 +200,7 @@ extern "C" h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cu
     const int e = dtype_bytes(dtype);
     const int64_t cs = rows > 1 ? cur_row_stride : hidden;
     const int64_t ps = rows > 1 ? prev_row_stride : hidden;
+    if (!extent_ok(rows, cs, hidden, e) || !extent_ok(rows, ps, hidden, e)) return H3F_ERR_UNSUPPORTED;
     const Region rc = region2d(cur, rows, cs, hidden, e);
     const Region rp = region2d(prev, rows, ps, hidden, e);
     if (!rows_separate(rc) || !rows_separate(rp)) return H3F_ERR_BAD_STRIDE;

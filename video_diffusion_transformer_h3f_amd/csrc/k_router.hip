@@ -519,26 +519,37 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
     const h3f_status_t st = check_plan(rows, heads, head_dim, block, sparsity, step);
     if (st != H3F_OK) return st;
     if (dtype != H3F_BF16) return H3F_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k)) return H3F_ERR_MISALIGNED;
-    if ((reinterpret_cast<uintptr_t>(kv_blocks) & 3u) || (reinterpret_cast<uintptr_t>(scores) & 3u))
-        return H3F_ERR_MISALIGNED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(scores)) return H3F_ERR_MISALIGNED;
+    if (reinterpret_cast<uintptr_t>(kv_blocks) & 3u) return H3F_ERR_MISALIGNED;
     constexpr int V = 8;
+    constexpr int64_t kMaxStride = int64_t(1) << 31;  // keeps every span product in range
+    if (std::max(q_row_stride, k_row_stride) > kMaxStride ||
+        (heads > 1 && std::max(q_head_stride, k_head_stride) > kMaxStride))
+        return H3F_ERR_UNSUPPORTED;
     if (q_row_stride % V || k_row_stride % V) return H3F_ERR_BAD_STRIDE;
     if (heads > 1 && (q_head_stride % V || k_head_stride % V || q_head_stride < head_dim ||
                       k_head_stride < head_dim))
         return H3F_ERR_BAD_STRIDE;
     const int64_t qhs = heads > 1 ? q_head_stride : head_dim;
     const int64_t khs = heads > 1 ? k_head_stride : head_dim;
+    if (!extent_ok(heads, qhs, head_dim, 2) || !extent_ok(heads, khs, head_dim, 2))
+        return H3F_ERR_UNSUPPORTED;
     const int64_t q_span = (int64_t)(heads - 1) * qhs + head_dim;
     const int64_t k_span = (int64_t)(heads - 1) * khs + head_dim;
+    if (!extent_ok(rows, q_row_stride, q_span, 2) || !extent_ok(rows, k_row_stride, k_span, 2))
+        return H3F_ERR_UNSUPPORTED;
     const Region rq = region2d(q, rows, q_row_stride, q_span, 2);
     const Region rk = region2d(k, rows, k_row_stride, k_span, 2);
     if (!rows_separate(rq) || !rows_separate(rk)) return H3F_ERR_BAD_STRIDE;
     // one block of rows (plus the rows an unrolled batch reads past its end,
     // which must stay outside the resource) is addressed with 32-bit offsets
-    if ((int64_t)(block + (kPoolUnroll + 1) * kPoolWaves) * std::max(q_row_stride, k_row_stride) * 2 +
-            2 * std::max(q_span, k_span) > 0xFFFFFFF0ll)
-        return H3F_ERR_UNSUPPORTED;
+    {
+        const int64_t span_bytes = 2 * std::max(q_span, k_span);
+        const int64_t block_rows = (int64_t)block + (kPoolUnroll + 1) * kPoolWaves;
+        if (span_bytes >= 0xFFFFFFF0ll ||
+            2 * std::max(q_row_stride, k_row_stride) > (0xFFFFFFF0ll - span_bytes - 1) / block_rows)
+            return H3F_ERR_UNSUPPORTED;
+    }
 
     const int64_t nb = (rows + block - 1) / block;
     const int64_t keep = keep_for(nb, sparsity, step);
