@@ -204,10 +204,13 @@ __device__ __forceinline__ void mfma_tile32_t(f32x4 (&acc)[2][2], const float (&
 // acc[m][n][e] = scores[i0 + 16 m + ri][j0 + 16 n + 4 g + e].  Stores go
 // through a buffer resource over the head's score matrix; an element outside
 // the matrix gets an offset past the resource's end and is dropped, so there
-// is no branch.  Rows start 16-byte aligned when nb % 4 == 0 (one 16-byte
-// store), 8-byte aligned when nb is even (two 8-byte stores), else 4 stores.
+// is no branch.  SB = bytes per store: 16 when rows start 16-byte aligned
+// (nb % 4 == 0), 8 when nb is even, else 4.  SB is a template parameter so
+// every tile issues a fixed number of stores, and the wait for the next
+// tile's operand loads never has to include this tile's stores.
 constexpr uint32_t kDropped = 0xFFFFFFF0u;
 
+template <int SB>
 __device__ __forceinline__ void store_tile32_t(rsrc_t r, uint32_t nb, uint32_t i0, uint32_t j0,
                                                int ri, int g, const f32x4 (&acc)[2][2]) {
 #pragma unroll
@@ -218,10 +221,10 @@ __device__ __forceinline__ void store_tile32_t(rsrc_t r, uint32_t nb, uint32_t i
             const uint32_t j = j0 + 16 * n + 4 * g;
             const uint32_t off = (i * nb + j) * 4u;
             const f32x4 v = acc[m][n];
-            if ((nb & 3u) == 0) {
+            if constexpr (SB == 16) {
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r,
                                                        i < nb && j < nb ? off : kDropped, 0, 0);
-            } else if ((nb & 1u) == 0) {
+            } else if constexpr (SB == 8) {
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
                     const u32x2 w = {__float_as_uint(v[2 * p]), __float_as_uint(v[2 * p + 1])};
@@ -238,6 +241,7 @@ __device__ __forceinline__ void store_tile32_t(rsrc_t r, uint32_t nb, uint32_t i
     }
 }
 
+template <int SB>
 __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
     const uint32_t runs = (a.tiles + kScoreRun - 1) / kScoreRun;
     const uint32_t per_head = a.tiles * runs;
@@ -274,7 +278,7 @@ __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
         // keep the next tile's loads ahead of this tile's matrix instructions
         __builtin_amdgcn_sched_barrier(0);
         mfma_tile32_t(acc, A, B[t & 1]);
-        store_tile32_t(ro, a.nb, i0, jbase + t * kTile, ri, g, acc);
+        store_tile32_t<SB>(ro, a.nb, i0, jbase + t * kTile, ri, g, acc);
     }
 }
 
@@ -596,9 +600,13 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
     sa.heads = heads;
     sa.nb = (uint32_t)nb;
     sa.tiles = (uint32_t)((nb + kTile - 1) / kTile);
-    hipLaunchKernelGGL(subblock_score_kernel,
-                       dim3((unsigned)(heads * sa.tiles * ((sa.tiles + kScoreRun - 1) / kScoreRun))),
-                       dim3(256), 0, s, sa);
+    const dim3 scg((unsigned)(heads * sa.tiles * ((sa.tiles + kScoreRun - 1) / kScoreRun)));
+    if (nb % 4 == 0)
+        hipLaunchKernelGGL(subblock_score_kernel<16>, scg, dim3(256), 0, s, sa);
+    else if (nb % 2 == 0)
+        hipLaunchKernelGGL(subblock_score_kernel<8>, scg, dim3(256), 0, s, sa);
+    else
+        hipLaunchKernelGGL(subblock_score_kernel<4>, scg, dim3(256), 0, s, sa);
 
     SelectArgs se;
     se.scores = scores;
