@@ -5,12 +5,12 @@
 // Three kernels, all deterministic (fixed summation order, no float atomics):
 //   pool    reads q and k once (the HBM-bound part: 2 * rows * heads * 256 B at
 //           head_dim 128) and writes fp32 block means to the workspace,
-//           [2][heads][n_blocks][128].  A workgroup owns one (tensor, block,
-//           group of 4 heads); lane (head hh, 8-element chunk c) walks the
-//           block's rows -- each wave load is one contiguous 1 KB row segment
-//           when heads are packed -- and sums in fp32 in row order; the waves
-//           of a workgroup split the rows round-robin and are added in wave
-//           order through LDS.
+//           [2][heads][n_blocks][128].  Dense q / k: one 128-thread workgroup
+//           per (tensor, block) streams the block's contiguous bytes front to
+//           back (flat form).  Other layouts: a workgroup owns one (tensor,
+//           block, group of 4 heads); lane (head hh, 8-element chunk c) walks
+//           the block's rows and the waves split the rows round-robin.  Sums
+//           are fp32 in a fixed order.
 //   score   scores[h] = Qm[h] Km[h]^T on the matrix cores (fp32 MFMA 16x16x4).
 //           A workgroup holds a 64-row tile of Qm in registers (32 x 32 per
 //           wave) and walks a run of 64-column tiles of Km with the next
@@ -47,9 +47,15 @@ constexpr int kMaxBlocks = 8192;
 #ifndef H3F_POOL_UNROLL
 #define H3F_POOL_UNROLL 8
 #endif
+#ifndef H3F_POOL_FLAT
+#define H3F_POOL_FLAT 1
+#endif
 constexpr int kPoolWaves = H3F_POOL_WAVES;
 constexpr int kPoolUnroll = H3F_POOL_UNROLL;
 constexpr int kHeadsPerGroup = 4;  // 4 heads x 16 lanes x 8 bf16 = one wave
+
+template <int P>
+constexpr int mult_max_slots();  // accumulator slots of a flat-pool workgroup (defined below)
 
 struct PoolArgs {
     const char* base[2];      // q, k
@@ -129,6 +135,93 @@ __global__ void __launch_bounds__(64 * WAVES) subblock_pool_kernel(PoolArgs a) {
     float* dst = a.pooled + (((size_t)t * a.heads + head) * a.n_blocks + b) * kHeadDim + c * 8;
     reinterpret_cast<float4*>(dst)[0] = m0;
     reinterpret_cast<float4*>(dst)[1] = m1;
+}
+
+// Flat form, for q / k whose rows and heads are packed ([rows, heads, 128]
+// dense): block b of a tensor is one contiguous range of nrows * cpr 16-byte
+// chunks (cpr = 16 * heads per row).  A workgroup of T = kFlatThreads threads
+// streams it front to back, T * 16 bytes per step; thread t takes chunks
+// t + T k.  Its column (t + T k) mod cpr repeats with period P = cpr /
+// gcd(T, cpr), so it keeps P accumulators and slot k mod P always meets the
+// same column.  The slots of all threads, L = t + T s (s < P), cover
+// [0, mult * cpr) exactly, with mult = T / gcd(T, cpr) copies of each column;
+// when mult > 1 the copies are added in copy order through LDS.  Fixed order
+// throughout.  Measured at the 5 s shape: 128 threads with 8 loads in flight
+// per thread beat 64-512 threads and 4-16 loads.
+#ifndef H3F_FLAT_THREADS
+#define H3F_FLAT_THREADS 128
+#endif
+#ifndef H3F_FLAT_DEPTH
+#define H3F_FLAT_DEPTH 8
+#endif
+constexpr int kFlatThreads = H3F_FLAT_THREADS;
+constexpr int kFlatDepth = H3F_FLAT_DEPTH;
+
+template <int P>
+constexpr int mult_max_slots() { return P * kFlatThreads; }
+
+template <int P>
+__global__ void __launch_bounds__(kFlatThreads) subblock_pool_flat_kernel(PoolArgs a, uint32_t cpr,
+                                                                          uint32_t mult) {
+    constexpr int U = P * ((kFlatDepth + P - 1) / P);  // loads in flight per thread, a multiple of P
+    __shared__ float part[mult_max_slots<P>()][8];
+    const uint32_t t = blockIdx.x >= a.n_blocks ? 1u : 0u;
+    const uint32_t b = blockIdx.x - t * a.n_blocks;
+    const uint32_t tid = threadIdx.x;
+    const int64_t r0 = (int64_t)b * a.block;
+    const int64_t nrows = std::min<int64_t>(a.block, a.rows - r0);
+    const uint32_t n_chunks = (uint32_t)nrows * cpr;
+    const rsrc_t rsrc = make_rsrc(a.base[t] + r0 * a.row_stride[t], n_chunks * 16u);
+    const uint32_t steps = (n_chunks + kFlatThreads - 1) / kFlatThreads;
+
+    float acc[P][8];
+#pragma unroll
+    for (int s = 0; s < P; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[s][i] = 0.f;
+    for (uint32_t k0 = 0; k0 < steps; k0 += U) {
+        Vec<__bf16, 8> v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)  // chunks past the block's end read as zeros
+            v[u].template load_buf<kLoadStream>(rsrc, (tid + kFlatThreads * (k0 + u)) * 16u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float f[8];
+            v[u].to_float(f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[u % P][i] += f[i];
+        }
+    }
+    const float n = (float)nrows;
+    float* out_t = a.pooled + (size_t)t * a.heads * a.n_blocks * kHeadDim;
+    auto store_mean = [&](uint32_t col, const float (&sum)[8]) {
+        const uint32_t head = col >> 4, d8 = col & 15u;
+        float* dst = out_t + ((size_t)head * a.n_blocks + b) * kHeadDim + d8 * 8;
+        float4 m0, m1;
+        m0.x = sum[0] / n; m0.y = sum[1] / n; m0.z = sum[2] / n; m0.w = sum[3] / n;
+        m1.x = sum[4] / n; m1.y = sum[5] / n; m1.z = sum[6] / n; m1.w = sum[7] / n;
+        reinterpret_cast<float4*>(dst)[0] = m0;
+        reinterpret_cast<float4*>(dst)[1] = m1;
+    };
+    if (mult == 1) {  // slot s of thread t is column t + kFlatThreads * s
+#pragma unroll
+        for (int s = 0; s < P; ++s) store_mean(tid + kFlatThreads * s, acc[s]);
+        return;
+    }
+#pragma unroll
+    for (int s = 0; s < P; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[tid + kFlatThreads * s][i] = acc[s][i];
+    __syncthreads();
+    for (uint32_t col = tid; col < cpr; col += kFlatThreads) {
+        float sum[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sum[i] = 0.f;
+        for (uint32_t c = 0; c < mult; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sum[i] += part[c * cpr + col][i];
+        store_mean(col, sum);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -591,8 +684,32 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
     pa.n_blocks = (uint32_t)nb;
     pa.n_groups = (uint32_t)((heads + kHeadsPerGroup - 1) / kHeadsPerGroup);
     pa.pooled = static_cast<float*>(workspace);
-    hipLaunchKernelGGL((subblock_pool_kernel<kPoolWaves, kPoolUnroll>),
-                       dim3(2 * pa.n_blocks * pa.n_groups), dim3(64 * kPoolWaves), 0, s, pa);
+    // flat streaming when both tensors are [rows, heads, 128] dense and a thread
+    // needs at most 8 accumulator slots
+    const uint32_t cpr = (uint32_t)heads * 16u;
+    uint32_t gcd = kFlatThreads, c2 = cpr;
+    while (c2) { const uint32_t r = gcd % c2; gcd = c2; c2 = r; }
+    const uint32_t P = cpr / gcd, mult = (uint32_t)kFlatThreads / gcd;
+    const bool dense = q_row_stride == (int64_t)heads * head_dim && k_row_stride == q_row_stride &&
+                       qhs == head_dim && khs == head_dim;
+    // the unrolled tail (at most 16 steps of 2 KiB) must stay within 32-bit offsets
+    const bool fits = (int64_t)block * cpr * 16 + (2 * kFlatDepth + 1) * kFlatThreads * 16 < 0xFFFFFFF0ll;
+    if (H3F_POOL_FLAT && dense && P <= 8 && fits) {
+        const dim3 fg(2 * pa.n_blocks), fb(kFlatThreads);
+        switch (P) {
+            case 1: hipLaunchKernelGGL(subblock_pool_flat_kernel<1>, fg, fb, 0, s, pa, cpr, mult); break;
+            case 2: hipLaunchKernelGGL(subblock_pool_flat_kernel<2>, fg, fb, 0, s, pa, cpr, mult); break;
+            case 3: hipLaunchKernelGGL(subblock_pool_flat_kernel<3>, fg, fb, 0, s, pa, cpr, mult); break;
+            case 4: hipLaunchKernelGGL(subblock_pool_flat_kernel<4>, fg, fb, 0, s, pa, cpr, mult); break;
+            case 5: hipLaunchKernelGGL(subblock_pool_flat_kernel<5>, fg, fb, 0, s, pa, cpr, mult); break;
+            case 6: hipLaunchKernelGGL(subblock_pool_flat_kernel<6>, fg, fb, 0, s, pa, cpr, mult); break;
+            case 7: hipLaunchKernelGGL(subblock_pool_flat_kernel<7>, fg, fb, 0, s, pa, cpr, mult); break;
+            default: hipLaunchKernelGGL(subblock_pool_flat_kernel<8>, fg, fb, 0, s, pa, cpr, mult); break;
+        }
+    } else {
+        hipLaunchKernelGGL((subblock_pool_kernel<kPoolWaves, kPoolUnroll>),
+                           dim3(2 * pa.n_blocks * pa.n_groups), dim3(64 * kPoolWaves), 0, s, pa);
+    }
 
     ScoreArgs sa;
     sa.pooled = pa.pooled;
