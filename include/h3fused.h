@@ -269,7 +269,9 @@ h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cur_row_strid
  * n_blocks > 8192, heads > 4096 or a stride above 2^31 elements;
  * H3F_ERR_BAD_VALUE for sparsity outside [0, 1) or step < 1;
  * H3F_ERR_BAD_SHAPE for block < 1 or heads < 1.
- * Deterministic: fixed summation order; bit-identical run to run.
+ * Deterministic: fixed summation order; bit-identical run to run.  -0 and +0
+ * scores rank equal; with non-finite q / k values the kept lists are still
+ * exactly keep valid, ascending block indices, but which ones is unspecified.
  */
 #define H3F_SUBBLOCK_FIRST_STEP 10
 h3f_status_t h3f_subblock_plan(int64_t rows, int32_t heads, int32_t head_dim, int32_t block,

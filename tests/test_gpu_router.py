@@ -166,11 +166,12 @@ def test_router_matches_oracle(rows, heads, block, packed, sparsity):
     print(f"  kept sets agree with the oracle's on {agree:.4%} of entries")
 
 
-def test_router_planted_scores_exact():
+@pytest.mark.parametrize("block", [128, 32])  # 33 blocks (sorted directly), 130 (probed first)
+def test_router_planted_scores_exact(block):
     # Every query token is e0; every token of key block j is alpha_j * e0 (head h
     # uses (-1)^h alpha).  Block means and scores are exact in fp32, so the kept
     # blocks must equal the oracle's exactly, ties included (alpha repeats).
-    rows, heads, block = 4096 + 40, 5, 128
+    rows, heads = 4096 + 40, 5
     nb = (rows + block - 1) // block
     rng = np.random.default_rng(11)
     alpha = rng.integers(-16, 17, size=nb).astype(np.float32) / 8.0   # many ties
@@ -188,6 +189,18 @@ def test_router_planted_scores_exact():
         kv_ref, sc_ref = oracle.subblock_route(qh, kh, block, sparsity, 12)
         assert np.array_equal(sc.astype(np.float64), sc_ref)
         assert np.array_equal(kv, kv_ref), f"sparsity {sparsity}"
+
+
+def test_router_all_scores_equal_keeps_lowest_blocks():
+    # zero queries: every score is +0 or -0 (0 times a negative mean), which rank
+    # equal, so each query block keeps the lowest-numbered key blocks
+    rows, heads, block = 8192 + 5, 3, 64
+    q = torch.zeros(rows, heads, 128, dtype=torch.bfloat16, device=DEV)
+    k = dev_tensor("k", rows, heads * 128, "bf16", seed=6).view(rows, heads, 128)
+    kv, sc = run_route(q, k, block, 0.8, step=10)
+    nb, keep = 129, 129 - int(0.8 * 129)
+    assert kv.shape == (heads, nb, keep) and (sc == 0).all()
+    assert (kv == np.arange(keep, dtype=np.int32)).all()
 
 
 def test_router_dense_steps_keep_everything():
