@@ -220,7 +220,7 @@ h3f_status_t h3f_gated_residual_adaln(void* x, h3f_dtype_t x_dtype, int64_t x_ro
  * workspace must be ordered on one stream.  Unlike the operators, rows == 0
  * is rejected (H3F_ERR_BAD_SHAPE): an empty tensor has no relative
  * difference.  If sum |prev| is 0, out[2] is inf or NaN (IEEE division).
- * Returns 0 from the size query for an invalid shape or type.
+ * Returns 0 from the size query for an invalid or unsupported shape or type.
  */
 size_t h3f_residual_l1_workspace_bytes(int64_t rows, int64_t hidden, h3f_dtype_t dtype);
 h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cur_row_stride,

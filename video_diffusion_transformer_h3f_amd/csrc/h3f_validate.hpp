@@ -87,8 +87,11 @@ inline bool alias_ok(const Region& out, const Region& other, bool same_type) {
 // Row footprint must not fold onto itself.
 inline bool rows_separate(const Region& r) { return r.rows <= 1 || r.stride >= r.span; }
 
+// ceil(n / d) for n >= 0, d >= 1, without the overflow of (n + d - 1) / d.
+inline int64_t ceil_div(int64_t n, int64_t d) { return n / d + (n % d != 0); }
+
 inline int64_t groups_for(int64_t rows, int64_t rows_per_group) {
-    return (rows + rows_per_group - 1) / rows_per_group;
+    return ceil_div(rows, rows_per_group);
 }
 
 }  // namespace h3f

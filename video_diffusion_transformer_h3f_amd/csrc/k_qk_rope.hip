@@ -236,8 +236,9 @@ h3f_status_t grid_args(const h3f_rope3d_t* r, int64_t rows, GridArgs& g) {
     }
     if (r->T < 1 || r->H < 1 || r->W < 1 || r->n_audio < 0) return H3F_ERR_BAD_SHAPE;
     if (r->token_offset < 0) return H3F_ERR_BAD_SHAPE;
-    const int64_t hw = (int64_t)r->H * r->W;
-    const int64_t nv = hw * r->T;
+    const int64_t hw = (int64_t)r->H * r->W;  // < 2^62: no overflow
+    if (hw > 0x7fffffffll) return H3F_ERR_UNSUPPORTED;
+    const int64_t nv = hw * r->T;              // < 2^62 once hw < 2^31
     const int64_t period = nv + r->n_audio;
     if (period > 0x7fffffffll) return H3F_ERR_UNSUPPORTED;
     const int64_t off = r->token_offset % period;

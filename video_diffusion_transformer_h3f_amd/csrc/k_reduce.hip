@@ -179,6 +179,7 @@ extern "C" size_t h3f_residual_l1_workspace_bytes(int64_t rows, int64_t hidden,
     if (rows <= 0 || hidden <= 0 || !dtype_ok(dtype)) return 0;
     const int V = vec_width(dtype == H3F_F32);
     if (hidden % V) return 0;
+    if (rows > 0x7fffffff || hidden / V > 0x7fffffff) return 0;  // sizes the call rejects
     return (size_t)n_partials(rows, hidden / V) * 2 * sizeof(double);
 }
 

@@ -580,9 +580,9 @@ h3f_status_t check_plan(int64_t rows, int32_t heads, int32_t head_dim, int32_t b
     if (rows < 0 || heads < 1 || block < 1 || head_dim < 1) return H3F_ERR_BAD_SHAPE;
     if (!(sparsity >= 0.0 && sparsity < 1.0) || step < 1) return H3F_ERR_BAD_VALUE;
     if (head_dim != kHeadDim || rows < kMinRows) return H3F_ERR_UNSUPPORTED;
-    if ((rows + block - 1) / block > kMaxBlocks || heads > 4096) return H3F_ERR_UNSUPPORTED;
+    if (ceil_div(rows, block) > kMaxBlocks || heads > 4096) return H3F_ERR_UNSUPPORTED;
     // a sparsity within rounding of 1 could leave no block at all
-    if (keep_for((rows + block - 1) / block, sparsity, step) < 1) return H3F_ERR_BAD_VALUE;
+    if (keep_for(ceil_div(rows, block), sparsity, step) < 1) return H3F_ERR_BAD_VALUE;
     return H3F_OK;
 }
 
@@ -597,7 +597,7 @@ extern "C" h3f_status_t h3f_subblock_plan(int64_t rows, int32_t heads, int32_t h
                                           size_t* workspace_bytes) {
     const h3f_status_t st = check_plan(rows, heads, head_dim, block, sparsity, step);
     if (st != H3F_OK) return st;
-    const int64_t nb = (rows + block - 1) / block;
+    const int64_t nb = ceil_div(rows, block);
     if (n_blocks) *n_blocks = (int32_t)nb;
     if (keep) *keep = (int32_t)keep_for(nb, sparsity, step);
     if (workspace_bytes) *workspace_bytes = workspace_for(nb, heads);
@@ -648,7 +648,7 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
             return H3F_ERR_UNSUPPORTED;
     }
 
-    const int64_t nb = (rows + block - 1) / block;
+    const int64_t nb = ceil_div(rows, block);
     const int64_t keep = keep_for(nb, sparsity, step);
     const size_t need = workspace_for(nb, heads);
     const bool routed = step >= H3F_SUBBLOCK_FIRST_STEP;
