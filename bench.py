@@ -17,8 +17,13 @@ workload (rank 0) as a baseline.  Outside the step, `extra_ops` times the
 step-reuse residual difference and the block-sparse attention router on the
 same shape.
 
+On the sweep shapes (tensors of a few hundred MB, comparable to the 256 MB
+Infinity Cache) a 1 GiB scratch buffer is written before every timed launch
+(--flush-mb), each launch is timed by its own event pair, and the step time is
+the sum of the launch times.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5s|10s|chain10s|sweepD]
-                       [--fused] [--no-cpu-baseline]
+                       [--fused] [--no-cpu-baseline] [--seed S] [--flush-mb M]
 """
 from __future__ import annotations
 
@@ -54,6 +59,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32768,
                     help="rows of the workload the oracle is timed on")
+    ap.add_argument("--seed", type=int, default=0, help="seed of the synthetic inputs")
+    ap.add_argument("--flush-mb", type=int, default=-1,
+                    help="MiB written to a scratch buffer before every timed launch, so no "
+                         "operand is served from the 256 MB Infinity Cache (default: 1024 for "
+                         "the sweep shapes, whose tensors are comparable to the cache; 0 "
+                         "otherwise)")
     return ap.parse_args()
 
 
@@ -105,7 +116,7 @@ def traffic_from_profiles(kernel_key, workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def build_inputs(c, N, torch, h3gen, dev, chain=False):
+def build_inputs(c, N, torch, h3gen, dev, chain=False, seed=0):
     D, F, H, Dh = c["D"], c["F"], c["heads"], c["Dh"]
     bf = torch.bfloat16
     xdt = torch.float32 if chain else bf
@@ -113,7 +124,7 @@ def build_inputs(c, N, torch, h3gen, dev, chain=False):
 
     def mk(name, rows, cols, dt, gen_name=None):
         x = torch.empty(rows, cols, dtype=dt, device=dev)
-        h3gen.fill_device(x, gen_name or name)
+        h3gen.fill_device(x, gen_name or name, seed=seed)
         return x
 
     t["x"] = mk("x", N, D, xdt)
@@ -126,7 +137,7 @@ def build_inputs(c, N, torch, h3gen, dev, chain=False):
         qkv = torch.empty(N, 3, H, Dh, dtype=bf, device=dev)
         flat = qkv.view(N, 3 * H * Dh)
         for i, n in enumerate(("q", "k", "v")):
-            h3gen.fill_device(flat[:, i * H * Dh:(i + 1) * H * Dh], n)
+            h3gen.fill_device(flat[:, i * H * Dh:(i + 1) * H * Dh], n, seed=seed)
         t["qkv"] = qkv
         t["q"], t["k"] = qkv[:, 0], qkv[:, 1]
     else:
@@ -166,7 +177,7 @@ def make_step(h3, t, rope, fused):
     ]
 
 
-def cpu_baseline(c, rows, x_bytes, min_seconds=10.0):
+def cpu_baseline(c, rows, x_bytes, min_seconds=10.0, seed=0):
     """Time the oracle on `rows` rows of the same workload (one block's six calls)."""
     import numpy as np
 
@@ -175,7 +186,7 @@ def cpu_baseline(c, rows, x_bytes, min_seconds=10.0):
 
     D, F, H, Dh = c["D"], c["F"], c["heads"], c["Dh"]
     xd = "f32" if x_bytes == 4 else "bf16"
-    g = lambda n, r, cols, dt="bf16": h3gen.host_rows(n, r, cols, dt)  # noqa: E731
+    g = lambda n, r, cols, dt="bf16": h3gen.host_rows(n, r, cols, dt, seed=seed)  # noqa: E731
     x = g("x", rows, D, xd)
     mods = {n: g(n, 1, D, xd) for n in ("shift", "scale", "gate", "shift2", "scale2", "gate2")}
     hh, hh2 = g("h", rows, D), g("h2", rows, D)
@@ -228,7 +239,32 @@ def main():
     c = GRIDS["10s" if chain else args.workload]
     N = c["T"] * c["H"] * c["W"] + c["A"]
     x_bytes = 4 if chain else 2
-    t = build_inputs(c, N, torch, h3gen, dev, chain=chain)
+    t = build_inputs(c, N, torch, h3gen, dev, chain=chain, seed=args.seed)
+    flush_mb = args.flush_mb if args.flush_mb >= 0 else (
+        1024 if args.workload.startswith("sweep") else 0)
+    scratch = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev) if flush_mb else None
+    flush = (lambda: scratch.fill_(1)) if flush_mb else None
+
+    def time_calls(fn, reps):
+        """Average ms of fn over reps launches: back to back, or each after a flush
+        with its own event pair (the flush is outside the timed interval)."""
+        if flush is None:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(reps)]
+        for a, b in pairs:
+            flush()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in pairs) / reps
     rope = h3.make_rope(c["T"], c["H"], c["W"], c["A"], c["split"])
     step = make_step(h3, t, rope, args.fused)
     if chain:
@@ -255,28 +291,39 @@ def main():
 
     K = args.steps
     n_ops = len(step)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ops + 1)] for _ in range(K)]
+    # event pairs around every launch; without a flush consecutive launches share
+    # their boundary event
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_ops)] for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
     for s in range(K):
-        ev[s][0].record()
         for i, (_, fn) in enumerate(step):
+            if flush is not None:
+                flush()
+            if flush is not None or i == 0:
+                ev[s][2 * i].record()
             fn()
-            ev[s][i + 1].record()
+            ev[s][2 * i + 1].record()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / K
+
+    def launch_ms(s, i):
+        first = ev[s][2 * i] if (flush is not None or i == 0) else ev[s][2 * i - 1]
+        return first.elapsed_time(ev[s][2 * i + 1])
 
     per_op_ms = {}
     per_op_n = {}
     for s in range(K):
         for i, (name, _) in enumerate(step):
-            per_op_ms[name] = per_op_ms.get(name, 0.0) + ev[s][i].elapsed_time(ev[s][i + 1])
+            per_op_ms[name] = per_op_ms.get(name, 0.0) + launch_ms(s, i)
             per_op_n[name] = per_op_n.get(name, 0) + 1
+    if flush is None:
+        ms_per_step = start.elapsed_time(stop) / K
+    else:  # the flushes between launches are not part of a step
+        ms_per_step = sum(launch_ms(s, i) for s in range(K) for i in range(n_ops)) / K
     step_bytes = sum(op_bytes(name, N, c, x_bytes) for name, _ in step)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     per_op = {}
@@ -298,13 +345,7 @@ def main():
         for _ in range(3):
             h3.h3f_residual_l1(l1_out, t["x"], x_prev, ws)
         torch.cuda.synchronize()
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        r0.record()
-        for _ in range(K):
-            h3.h3f_residual_l1(l1_out, t["x"], x_prev, ws)
-        r1.record()
-        torch.cuda.synchronize()
-        avg = r0.elapsed_time(r1) / K
+        avg = time_calls(lambda: h3.h3f_residual_l1(l1_out, t["x"], x_prev, ws), K)
         b = 2 * N * c["D"] * 2
         extra_ops["residual_l1"] = {"avg_ms": round(avg, 4), "bytes": b,
                                     "GBps": round(b / (avg * 1e-3) / 1e9, 1),
@@ -321,13 +362,8 @@ def main():
         for _ in range(3):
             h3.h3f_subblock_route(kv, sc, t["q_out"], t["k_out"], blk, sp, 10, ws)
         torch.cuda.synchronize()
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        r0.record()
-        for _ in range(K):
-            h3.h3f_subblock_route(kv, sc, t["q_out"], t["k_out"], blk, sp, 10, ws)
-        r1.record()
-        torch.cuda.synchronize()
-        avg = r0.elapsed_time(r1) / K
+        avg = time_calls(lambda: h3.h3f_subblock_route(kv, sc, t["q_out"], t["k_out"], blk, sp,
+                                                       10, ws), K)
         b = router_bytes(N, c, nb, keep)
         extra_ops["subblock_route"] = {
             "avg_ms": round(avg, 4), "bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1),
@@ -345,7 +381,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(c, min(args.cpu_rows, N), x_bytes)
+        cpu = cpu_baseline(c, min(args.cpu_rows, N), x_bytes, seed=args.seed)
 
     wl = {"5s": "5 s 1344x768 clip token shape", "10s": "10 s 1344x768 clip token shape",
           "chain10s": "10 s shape, fp32 residual stream, packed qkv, block epilogue chain"}
@@ -377,6 +413,8 @@ def main():
         "per_op": per_op,
         "extra_ops": extra_ops,
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "cache_flush_mb": flush_mb,
+        "seed": args.seed,
         "wall_s_timed_region": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
