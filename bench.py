@@ -331,7 +331,8 @@ def main():
         avg = per_op_ms[name] / per_op_n[name]
         b = op_bytes(name, N, c, x_bytes)
         per_op[name] = {"avg_ms": round(avg, 4), "bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1),
-                        "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+                        "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                        "frac_of_copy_ceiling": round(b / (avg * 1e-3) / 1e9 / copy_gbps, 4)}
 
     # Step-reuse test (residual difference between neighbouring steps): timed on its
     # own, outside the block step, since a block runs it at most once per step.
