@@ -76,6 +76,8 @@ def _declare(L):
     L.oracle_positions.argtypes = [_p, _i64, _i64, _i32, _i32, _i32, _i32]
     L.oracle_adaln_modulate.argtypes = [_p, _int, _p, _int, _p, _p, _int, _p,
                                         _i64, _i64, _i64, _f]
+    L.oracle_adaln_affine_modulate.argtypes = [_p, _int, _p, _int, _p, _p, _p, _p, _int, _p,
+                                               _i64, _i64, _i64, _f]
     L.oracle_gated_residual.argtypes = [_p, _int, _p, _int, _p, _p, _i64, _i64, _i64]
     L.oracle_swiglu.argtypes = [_p, _p, _int, _i64, _i64]
     L.oracle_rope_inv_freq.argtypes = [_p, _i32, _i32, _i32, _d]
@@ -166,6 +168,27 @@ def adaln_modulate(x, shift, scale, eps=1e-6, y_dtype=None, group=None,
     lib().oracle_adaln_modulate(_ptr(y), _dt(y), _ptr(x), _dt(x), _ptr(shift),
                                 _ptr(scale), _dt(shift), _ptr(g), max(rpg, 1),
                                 rows, D, eps)
+    return y
+
+
+def adaln_affine_modulate(x, gamma, beta, shift, scale, eps=1e-6, y_dtype=None, group=None,
+                          rows_per_group=None):
+    """y = (LN(x) * gamma + beta) * (1 + scale[g]) + shift[g]; gamma, beta [D]."""
+    x = np.ascontiguousarray(x)
+    rows, D = x.shape
+    gamma = np.ascontiguousarray(gamma).reshape(D)
+    beta = np.ascontiguousarray(beta).reshape(D)
+    shift = np.ascontiguousarray(shift).reshape(-1, D)
+    scale = np.ascontiguousarray(scale).reshape(-1, D)
+    for v in (beta, shift, scale):
+        assert v.dtype == gamma.dtype
+    ydt = x.dtype if y_dtype is None else np.dtype(y_dtype)
+    y = np.zeros((rows, D), dtype=ydt)
+    g = _groups(group, rows)
+    rpg = rows if rows_per_group is None else rows_per_group
+    lib().oracle_adaln_affine_modulate(_ptr(y), _dt(y), _ptr(x), _dt(x), _ptr(gamma), _ptr(beta),
+                                       _ptr(shift), _ptr(scale), _dt(shift), _ptr(g),
+                                       max(rpg, 1), rows, D, eps)
     return y
 
 

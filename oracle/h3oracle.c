@@ -145,6 +145,45 @@ void oracle_adaln_modulate(void* y, int y_dtype, const void* x, int x_dtype,
 }
 
 /* ---------------------------------------------------------------------------
+ * LayerNorm with its own affine gain and bias (Ba, Kiros & Hinton 2016, eq. 4:
+ * g * (a - mean) / sigma + b), then the AdaLN modulation of that output.  A
+ * variant of the reading above for models whose LayerNorm keeps its affine
+ * parameters; gamma and beta are [hidden], shared by every row and group.
+ * ------------------------------------------------------------------------- */
+static void adaln_affine_row(void* y, int y_dtype, const void* x, int x_dtype,
+                             const void* gamma, const void* beta,
+                             const void* shift, const void* scale, int mod_dtype,
+                             int64_t r, int64_t g, int64_t D, double eps) {
+    double sum = 0.0;
+    for (int64_t c = 0; c < D; ++c) sum += ld(x, x_dtype, r * D + c);
+    const double mean = sum / (double)D;
+    double ss = 0.0;
+    for (int64_t c = 0; c < D; ++c) {
+        const double d = ld(x, x_dtype, r * D + c) - mean;
+        ss += d * d;
+    }
+    const double sigma = sqrt(ss / (double)D + eps);
+    for (int64_t c = 0; c < D; ++c) {
+        const double ln = ld(gamma, mod_dtype, c) * (ld(x, x_dtype, r * D + c) - mean) / sigma +
+                          ld(beta, mod_dtype, c);
+        const double sc = ld(scale, mod_dtype, g * D + c);
+        const double sh = ld(shift, mod_dtype, g * D + c);
+        st(y, y_dtype, r * D + c, ln * (1.0 + sc) + sh);
+    }
+}
+
+void oracle_adaln_affine_modulate(void* y, int y_dtype, const void* x, int x_dtype,
+                                  const void* gamma, const void* beta,
+                                  const void* shift, const void* scale, int mod_dtype,
+                                  const int64_t* group, int64_t rows_per_group,
+                                  int64_t rows, int64_t hidden, float eps) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        adaln_affine_row(y, y_dtype, x, x_dtype, gamma, beta, shift, scale, mod_dtype, r,
+                         group_of(group, rows_per_group, r), hidden, (double)eps);
+}
+
+/* ---------------------------------------------------------------------------
  * Gated residual.  Named in the report page's section "Só com três
  * camadas…" (residual with gate).  Definition: the DiT block's gated
  * residual, x <- x + alpha * h, alpha broadcast over tokens like the AdaLN

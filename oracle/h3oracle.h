@@ -83,6 +83,16 @@ void oracle_adaln_modulate(void* y, int y_dtype, const void* x, int x_dtype,
                            const int64_t* group, int64_t rows_per_group,
                            int64_t rows, int64_t hidden, float eps);
 
+/* --- AdaLN modulate over a LayerNorm with affine parameters ------------------
+ * y[r,:] = (gamma * (x[r,:] - mean) / sqrt(var + eps) + beta) * (1 + scale[g,:])
+ *          + shift[g,:]
+ * gamma, beta: [hidden] of mod_dtype, shared by all rows; the rest as above. */
+void oracle_adaln_affine_modulate(void* y, int y_dtype, const void* x, int x_dtype,
+                                  const void* gamma, const void* beta,
+                                  const void* shift, const void* scale, int mod_dtype,
+                                  const int64_t* group, int64_t rows_per_group,
+                                  int64_t rows, int64_t hidden, float eps);
+
 /* --- gated residual ---------------------------------------------------------
  * x[r,:] = x[r,:] + gate[g,:] * h[r,:]   (in place; gate has x's type) */
 void oracle_gated_residual(void* x, int x_dtype, const void* h, int h_dtype,

@@ -38,6 +38,9 @@ MUTANTS = {
     "audio_position_axis": ("t = (int32_t)(p - n_video);\n            h = 0;",
                             "t = 0;\n            h = (int32_t)(p - n_video);"),
     "bf16_round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u + 0 * lsb;"),
+    "affine_after_modulation": ("st(y, y_dtype, r * D + c, ln * (1.0 + sc) + sh);",
+                                "st(y, y_dtype, r * D + c, (ln - ld(beta, mod_dtype, c)) * (1.0 + sc) + sh + ld(beta, mod_dtype, c));"),
+    "affine_gamma_beta_swapped": ("const double ln = ld(gamma, mod_dtype, c) *", "const double ln = ld(beta, mod_dtype, c) *"),
     "subblock_sum_not_mean": ("= s / (double)(r1 - r0);", "= s;"),
     "subblock_full_block_divisor": ("= s / (double)(r1 - r0);", "= s / (double)block;"),
     "subblock_wrong_head": ("ld(x, dtype, (r * heads + h) * head_dim + d)",

@@ -157,6 +157,37 @@ def test_adaln_scale_minus_one_gives_shift_exactly():
     assert np.array_equal(yb, np.broadcast_to(shb, yb.shape))
 
 
+def test_adaln_affine_zero_modulation_is_layer_norm_with_weight_and_bias():
+    x = f32(RNG.standard_normal((29, 192)) * 2 + 0.3)
+    gamma = f32(1 + RNG.standard_normal(192) * 0.2)
+    beta = f32(RNG.standard_normal(192) * 0.3)
+    zero = f32(np.zeros((1, 192)))
+    y = as_f64(oracle.adaln_affine_modulate(x, gamma, beta, zero, zero, eps=1e-6))
+    ref = torch.nn.functional.layer_norm(
+        torch.from_numpy(x.astype(np.float64)), (192,),
+        weight=torch.from_numpy(gamma.astype(np.float64)),
+        bias=torch.from_numpy(beta.astype(np.float64)), eps=float(np.float32(1e-6))).numpy()
+    assert np.max(np.abs(y - ref.astype(np.float32).astype(np.float64)) / ulp_f32(ref)) <= 1.0
+
+
+def test_adaln_affine_order_and_degenerate_parameters():
+    x = f32(RNG.standard_normal((7, 64)))
+    gamma = f32(1 + RNG.standard_normal(64) * 0.2)
+    beta = f32(RNG.standard_normal(64))
+    sh = f32(RNG.standard_normal((1, 64)))
+    sc = f32(RNG.standard_normal((1, 64)) * 0.3)
+    # the modulation acts on the affine LayerNorm output: scale = -1 leaves exactly shift
+    y = oracle.adaln_affine_modulate(x, gamma, beta, sh, f32(-np.ones((1, 64))))
+    assert np.array_equal(y, np.broadcast_to(sh, y.shape))
+    # gamma = 0 leaves beta (1 + scale) + shift, whatever x is
+    y0 = as_f64(oracle.adaln_affine_modulate(x, f32(np.zeros(64)), beta, sh, sc))
+    want = beta.astype(np.float64) * (1 + sc.astype(np.float64)) + sh.astype(np.float64)
+    assert np.max(np.abs(y0 - want) / ulp_f32(want)) <= 1.0
+    # gamma = 1, beta = 0 is the plain AdaLN modulate
+    y1 = oracle.adaln_affine_modulate(x, f32(np.ones(64)), f32(np.zeros(64)), sh, sc)
+    assert np.array_equal(y1, oracle.adaln_modulate(x, sh, sc))
+
+
 def test_adaln_bf16_output_is_rounded_f32_output():
     x = f32(RNG.standard_normal((11, 96)))
     sh = f32(RNG.standard_normal((1, 96)) * 0.1)
