@@ -25,6 +25,7 @@ TENSOR_IDS = {
     "x": 1, "shift": 2, "scale": 3, "gate": 4, "h": 5, "gate_up": 6,
     "q": 7, "k": 8, "v": 9, "q_weight": 10, "k_weight": 11,
     "shift2": 12, "scale2": 13, "gate2": 14, "h2": 15, "x_prev": 16,
+    "ln_gamma": 17, "ln_beta": 18,
 }
 
 # Value distributions of the synthetic workload (mean, standard deviation).
@@ -34,6 +35,7 @@ DISTRIBUTIONS = {
     "shift": (0.0, 0.1), "scale": (0.0, 0.1), "shift2": (0.0, 0.1), "scale2": (0.0, 0.1),
     "gate": (0.0, 0.5), "gate2": (0.0, 0.5),
     "q_weight": (1.0, 0.05), "k_weight": (1.0, 0.05),
+    "ln_gamma": (1.0, 0.05), "ln_beta": (0.0, 0.1),
 }
 
 _host = None

@@ -140,6 +140,22 @@ h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t y_row_stri
                                 void* stream);
 
 /*
+ * AdaLN modulate over a LayerNorm that keeps its own affine gain and bias
+ * (Ba, Kiros & Hinton 2016, eq. 4), for models whose LayerNorm is not
+ * affine-free:
+ *   y[r,:] = (gamma * (x[r,:] - mean_r) / sqrt(var_r + eps) + beta)
+ *            * (1 + scale[g,:]) + shift[g,:]
+ * gamma, beta: [hidden] of x_dtype, 16-byte aligned, shared by every row and
+ * group; they must not overlap y.  Everything else as h3f_adaln_modulate.
+ */
+h3f_status_t h3f_adaln_affine_modulate(void* y, h3f_dtype_t y_dtype, int64_t y_row_stride,
+                                       const void* x, h3f_dtype_t x_dtype, int64_t x_row_stride,
+                                       const void* gamma, const void* beta, const void* shift,
+                                       const void* scale, int64_t mod_group_stride,
+                                       int64_t rows_per_group, int64_t rows, int64_t hidden,
+                                       float eps, void* stream);
+
+/*
  * Gated residual (the report's "residual com gate"), in place:
  *   x[r,:] = x[r,:] + gate[g,:] * h[r,:]
  *   x: [rows, hidden] of x_dtype (read and written); h: [rows, hidden] of

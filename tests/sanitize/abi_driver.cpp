@@ -47,6 +47,13 @@ int main() {
                               nullptr), H3F_ERR_UNSUPPORTED);
     EXPECT(h3f_adaln_modulate(A(0), B, 512, A(1), B, 512, A(2), A(3), huge & ~int64_t(7), 1, 10,
                               512, 1e-6f, nullptr), H3F_ERR_UNSUPPORTED);
+    EXPECT(h3f_adaln_affine_modulate(A(0), B, 512, A(1), B, big, A(6), A(7), A(2), A(3), 0, 4,
+                                     10, 512, 1e-6f, nullptr), H3F_ERR_UNSUPPORTED);
+    EXPECT(h3f_adaln_affine_modulate(A(0), B, 512, A(1), B, 512, nullptr, A(7), A(2), A(3), 0, 4,
+                                     10, 512, 1e-6f, nullptr), H3F_ERR_NULL_POINTER);
+    EXPECT(h3f_adaln_affine_modulate(A(0), B, 512, A(1), B, 512, A(6), A(7), A(2), A(3),
+                                     huge & ~int64_t(7), 1, 10, 512, 1e-6f, nullptr),
+           H3F_ERR_UNSUPPORTED);
     EXPECT(h3f_gated_residual_adaln(A(0), F, 512, A(1), B, big, A(2), A(3), A(4), 0, 4, A(5), B,
                                     512, 10, 512, 1e-6f, nullptr), H3F_ERR_UNSUPPORTED);
     // QK RMSNorm + RoPE

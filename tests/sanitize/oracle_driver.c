@@ -49,6 +49,10 @@ int main(void) {
                           rows, D, 1e-6f);
     oracle_adaln_modulate(yb, ORACLE_BF16, xb, ORACLE_BF16, modb, modb + G * D, ORACLE_BF16, NULL,
                           rpg, rows, D, 1e-6f);
+    oracle_adaln_affine_modulate(y, ORACLE_F32, x, ORACLE_F32, mod + 2 * G * D, mod + 2 * G * D,
+                                 mod, mod + G * D, ORACLE_F32, NULL, rpg, rows, D, 1e-6f);
+    oracle_adaln_affine_modulate(yb, ORACLE_BF16, xb, ORACLE_BF16, modb + 2 * G * D, modb,
+                                 modb, modb + G * D, ORACLE_BF16, grp, 1, rows, D, 1e-6f);
     oracle_gated_residual(x, ORACLE_F32, hb, ORACLE_BF16, mod, NULL, rpg, rows, D);
     oracle_gated_residual(xb, ORACLE_BF16, hb, ORACLE_BF16, modb, grp, 1, rows, D);
     oracle_gated_residual_adaln(x, ORACLE_F32, h, ORACLE_F32, mod, yb, ORACLE_BF16,

@@ -341,3 +341,21 @@ def test_absurd_strides_are_rejected_without_overflow():
     assert qk(krs=big) == UNSUP
     assert L.h3f_residual_l1(A(0), A(1), big, A(2), 512, BF16, 4, 512, A(3), 1 << 20,
                              None) == UNSUP
+
+
+def test_adaln_affine_validation():
+    def aff(y=A(0), yd=BF16, ys=512, x=A(1), xd=BF16, xs=512, gm=A(4), bt=P(0x50000000 + 4096),
+            sh=A(2), sc=A(3), gs=0, rpg=8, rows=8, hidden=512):
+        return L.h3f_adaln_affine_modulate(y, yd, ys, x, xd, xs, gm, bt, sh, sc, gs, rpg, rows,
+                                           hidden, ctypes.c_float(1e-6), None)
+
+    assert aff(gm=None, rows=0) == OK
+    assert aff(gm=None) == NULLP
+    assert aff(bt=None) == NULLP
+    assert aff(xd=F32, yd=F32, hidden=16384) == UNSUP
+    assert aff(gm=P(0x50000008)) == MISAL
+    assert aff(bt=P(0x50000000 + 4100)) == MISAL
+    assert aff(gm=P(0x10000000 + 64)) == ALIAS   # gamma inside y
+    assert aff(bt=P(0x10000000 + 512)) == ALIAS  # beta inside y
+    assert aff(yd=F32) == DTYPE
+    assert aff(hidden=500) == SHAPE

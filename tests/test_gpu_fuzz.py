@@ -135,6 +135,27 @@ def test_fuzz_gated_residual_adaln(case):
     assert_close(to_np(y), ry, kind(yd), f"fused y case {case}")
 
 
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_fuzz_adaln_affine(case):
+    r = np.random.default_rng(8000 + case)
+    xd, yd = DT_PAIRS[int(r.integers(3))]
+    V = width(xd, yd)
+    max_d = 8192 if xd == "f32" else 16384
+    rows, D = int(r.integers(1, 400)), V * int(r.integers(1, max_d // V + 1))
+    rpg, groups = grouping(r, rows)
+    print(f"adaln affine case {case}: rows={rows} D={D} {xd}->{yd} rpg={rpg}", flush=True)
+    x = dev_tensor("x", rows, D, xd, row_stride=D + V * int(r.integers(0, 4)))
+    gm, bt = dev_tensor("ln_gamma", 1, D, xd).view(D), dev_tensor("ln_beta", 1, D, xd).view(D)
+    sh, sc = dev_tensor("shift", groups, D, xd), dev_tensor("scale", groups, D, xd)
+    y = torch.empty(rows, D, dtype=tdt(yd), device=DEV)
+    h3.h3f_adaln_affine_modulate(y, x, gm, bt, sh, sc, eps=1e-6, rows_per_group=rpg)
+    ref = oracle.adaln_affine_modulate(host("x", rows, D, xd), host("ln_gamma", 1, D, xd),
+                                       host("ln_beta", 1, D, xd), host("shift", groups, D, xd),
+                                       host("scale", groups, D, xd), eps=1e-6, y_dtype=npy(yd),
+                                       rows_per_group=rpg)
+    assert_close(to_np(y), ref, kind(yd), f"adaln affine case {case}")
+
+
 SPLITS = {32: (8, 8, 16), 64: (16, 24, 24), 128: (32, 48, 48), 256: (64, 96, 96)}
 
 

@@ -186,6 +186,47 @@ def test_adaln(case):
     assert_close(to_np(y), ref, kind(yd), "adaln")
 
 
+ADALN_AFFINE_CASES = [
+    # rows, hidden, x dtype, y dtype, groups
+    (112, 256, "f32", "f32", 1),
+    (1001, 5120, "bf16", "bf16", 1),    # modulation and gamma/beta staged in LDS
+    (513, 5120, "f32", "bf16", 3),      # read through the caches
+    (65, 16384, "bf16", "bf16", 1),     # too large to stage
+    (300, 3072, "bf16", "bf16", 300),   # per-token modulation
+    (17, 4, "f32", "f32", 1),
+]
+
+
+@pytest.mark.parametrize("case", ADALN_AFFINE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_adaln_affine(case):
+    rows, D, xd, yd, groups = case
+    x = dev_tensor("x", rows, D, xd)
+    gm, bt = dev_tensor("ln_gamma", 1, D, xd).view(D), dev_tensor("ln_beta", 1, D, xd).view(D)
+    sh = dev_tensor("shift", groups, D, xd)
+    sc = dev_tensor("scale", groups, D, xd)
+    y = torch.empty(rows, D, dtype=torch.bfloat16 if yd == "bf16" else torch.float32, device=DEV)
+    rpg = -(-rows // groups)
+    h3.h3f_adaln_affine_modulate(y, x, gm, bt, sh, sc, eps=1e-6, rows_per_group=rpg)
+    ref = oracle.adaln_affine_modulate(host("x", rows, D, xd), host("ln_gamma", 1, D, xd),
+                                       host("ln_beta", 1, D, xd), host("shift", groups, D, xd),
+                                       host("scale", groups, D, xd), eps=1e-6,
+                                       y_dtype=np.uint16 if yd == "bf16" else np.float32,
+                                       rows_per_group=rpg)
+    assert_close(to_np(y), ref, kind(yd), "adaln affine")
+
+
+def test_adaln_affine_identity_parameters_match_plain_adaln():
+    # gamma = 1, beta = 0: bit-identical to the plain operator
+    rows, D = 257, 5120
+    x = dev_tensor("x", rows, D, "bf16")
+    sh, sc = dev_tensor("shift", 1, D, "bf16"), dev_tensor("scale", 1, D, "bf16")
+    y0, y1 = torch.empty_like(x), torch.empty_like(x)
+    h3.h3f_adaln_modulate(y0, x, sh, sc)
+    h3.h3f_adaln_affine_modulate(y1, x, torch.ones(D, dtype=torch.bfloat16, device=DEV),
+                                 torch.zeros(D, dtype=torch.bfloat16, device=DEV), sh, sc)
+    assert torch.equal(y0, y1)
+
+
 def test_adaln_in_place_strided_and_offset_rows():
     rows, D = 400, 5120
     x = dev_tensor("x", rows, D, "bf16", row_stride=D + 128)
@@ -236,7 +277,7 @@ def test_gated_residual_adaln(case):
 # ------------------------------------------------------------------------------------
 
 def _qk_case(cfg, dtype, rows, offset=0, pairing=h3.H3F_ROPE_INTERLEAVED, packed=False,
-             in_place=False, positions=False):
+             in_place=False, positions=False, audio_aligned=False):
     H, Dh = cfg["heads"], cfg["Dh"]
     if packed:
         qkv = torch.empty(rows, 3, H, Dh, dtype=torch.bfloat16 if dtype == "bf16" else
@@ -259,6 +300,14 @@ def _qk_case(cfg, dtype, rows, offset=0, pairing=h3.H3F_ROPE_INTERLEAVED, packed
     refk = host("k", ids, H * Dh, dtype).reshape(rows, H, Dh)
     v_before = to_np(qkv[:, 2]) if packed else None
     pos_np = oracle.positions(rows, cfg["T"], cfg["H"], cfg["W"], cfg["A"], token_offset=offset)
+    if audio_aligned:
+        # the other reading of the audio axis: audio token k shares the time index of
+        # the video frame it plays under, t = floor(k * T / n_audio), at h = w = 0
+        n_video = cfg["T"] * cfg["H"] * cfg["W"]
+        p = (offset + np.arange(rows)) % (n_video + cfg["A"])
+        audio = p >= n_video
+        pos_np[audio, 0] = (p[audio] - n_video) * cfg["T"] // cfg["A"]
+        assert audio.any() and (pos_np[audio, 1:] == 0).all()
     pos_t = from_np(pos_np) if positions else None
     rope = h3.make_rope(cfg["T"], cfg["H"], cfg["W"], cfg["A"], cfg["split"],
                         token_offset=0 if positions else offset, positions=pos_t,
@@ -312,6 +361,12 @@ def test_qk_packed_strided_out_of_place():
 
 def test_qk_explicit_positions():
     _qk_case(S5, "bf16", 150, offset=124900, positions=True)
+
+
+def test_qk_explicit_positions_audio_aligned_to_frames():
+    # explicit positions carry a different audio placement through the same kernel
+    n_video = S5["T"] * S5["H"] * S5["W"]
+    _qk_case(S5, "bf16", 400, offset=n_video - 200, positions=True, audio_aligned=True)
 
 
 def test_qk_half_split_pairing():

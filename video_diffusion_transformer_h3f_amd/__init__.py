@@ -34,7 +34,7 @@ EXPORTS = [
     "h3f_abi_version", "h3f_status_string", "h3f_rope3d_positions", "h3f_adaln_modulate",
     "h3f_gated_residual", "h3f_swiglu", "h3f_qk_rmsnorm_rope3d", "h3f_gated_residual_adaln",
     "h3f_stream_copy", "h3f_residual_l1_workspace_bytes", "h3f_residual_l1",
-    "h3f_subblock_plan", "h3f_subblock_route",
+    "h3f_subblock_plan", "h3f_subblock_route", "h3f_adaln_affine_modulate",
 ]
 
 
@@ -74,6 +74,8 @@ def lib():
         L.h3f_status_string.restype = ctypes.c_char_p
         L.h3f_rope3d_positions.argtypes = [p, i64, ctypes.POINTER(Rope3D), p]
         L.h3f_adaln_modulate.argtypes = [p, st, i64, p, st, i64, p, p, i64, i64, i64, i64, f, p]
+        L.h3f_adaln_affine_modulate.argtypes = [p, st, i64, p, st, i64, p, p, p, p, i64, i64,
+                                                i64, i64, f, p]
         L.h3f_gated_residual.argtypes = [p, st, i64, p, st, i64, p, i64, i64, i64, i64, p]
         L.h3f_swiglu.argtypes = [p, i64, p, i64, p, i64, st, i64, i64, p]
         L.h3f_qk_rmsnorm_rope3d.argtypes = [p, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64,
@@ -200,6 +202,28 @@ def h3f_adaln_modulate(y, x, shift, scale, eps: float = 1e-6, rows_per_group=Non
     _check("h3f_adaln_modulate", lib().h3f_adaln_modulate(
         _ptr(y), _dtype(y), ys, _ptr(x), _dtype(x), xs, _ptr(shift), _ptr(scale), gs, rpg, rows,
         hidden, eps, _stream(dev, stream)))
+    return y
+
+
+def h3f_adaln_affine_modulate(y, x, gamma, beta, shift, scale, eps: float = 1e-6,
+                              rows_per_group=None, stream=None):
+    """y[r] = (LN(x[r]) * gamma + beta) * (1 + scale[g]) + shift[g]; gamma, beta [hidden]."""
+    dev = _dev(y, x, gamma, beta, shift, scale)
+    rows, hidden, xs = _rows2d(x, "x")
+    yr, yh, ys = _rows2d(y, "y")
+    if (yr, yh) != (rows, hidden):
+        raise ValueError("y and x shapes differ")
+    for v, n in ((gamma, "gamma"), (beta, "beta")):
+        if v.numel() != hidden or not v.is_contiguous():
+            raise ValueError(f"{n}: expected a contiguous [hidden] tensor")
+    groups, gs = _mod(shift, hidden, "shift")
+    g2, gs2 = _mod(scale, hidden, "scale")
+    if (groups, gs) != (g2, gs2):
+        raise ValueError("shift and scale must share shape and strides")
+    rpg = _rows_per_group(rows, groups, rows_per_group)
+    _check("h3f_adaln_affine_modulate", lib().h3f_adaln_affine_modulate(
+        _ptr(y), _dtype(y), ys, _ptr(x), _dtype(x), xs, _ptr(gamma), _ptr(beta), _ptr(shift),
+        _ptr(scale), gs, rpg, rows, hidden, eps, _stream(dev, stream)))
     return y
 
 

@@ -38,6 +38,8 @@ struct AdalnArgs {
     const void* gate;
     const void* shift;
     const void* scale;
+    const void* gamma;  // LayerNorm affine gain and bias, [hidden], shared by all rows
+    const void* beta;
     int64_t mod_gs;  // bytes
     FastDiv div_group;
     int64_t rows;
@@ -53,7 +55,7 @@ struct ModSource {
     static constexpr int Q = Vec<TX, VEC>::kQuads;
     const u32x4* lds;  // [n_vectors][nvec * Q]
     int32_t nvec;
-    rsrc_t r[3];
+    rsrc_t r[4];
     __device__ __forceinline__ void get(int which, uint32_t c, Vec<TX, VEC>& v) const {
         if constexpr (LDSMOD) {
 #pragma unroll
@@ -66,13 +68,16 @@ struct ModSource {
 
 extern __shared__ u32x4 adaln_lds[];
 
-template <typename TX, typename TY, typename TH, int VEC, int NV, bool FUSED, bool LDSMOD>
+// Vectors read per row: shift, scale, then gate (FUSED) or gamma, beta (AFFINE).
+template <typename TX, typename TY, typename TH, int VEC, int NV, bool FUSED, bool LDSMOD,
+          bool AFFINE>
 __global__ void __launch_bounds__(kWaves * 64) adaln_kernel(AdalnArgs a) {
+    static_assert(!(FUSED && AFFINE), "the fused form has no LayerNorm affine");
     constexpr int Q = Vec<TX, VEC>::kQuads;
-    constexpr int NMOD = FUSED ? 3 : 2;  // (gate,) shift, scale
+    constexpr int NMOD = FUSED ? 3 : (AFFINE ? 4 : 2);
     const int lane = threadIdx.x & 63;
     const uint32_t xrow_bytes = (uint32_t)a.hidden * sizeof(TX);
-    const void* mods[3] = {a.shift, a.scale, a.gate};
+    const void* mods[4] = {a.shift, a.scale, FUSED ? a.gate : a.gamma, a.beta};
 
     ModSource<TX, VEC, LDSMOD> ms;
     ms.nvec = a.nvec;
@@ -92,8 +97,11 @@ __global__ void __launch_bounds__(kWaves * 64) adaln_kernel(AdalnArgs a) {
     const uint32_t grp = fdiv((uint32_t)row, a.div_group);
     if constexpr (!LDSMOD) {
 #pragma unroll
-        for (int m = 0; m < NMOD; ++m)
-            ms.r[m] = make_rsrc(static_cast<const char*>(mods[m]) + grp * a.mod_gs, xrow_bytes);
+        for (int m = 0; m < NMOD; ++m) {
+            const bool shared = AFFINE && m >= 2;  // gamma, beta: one row for every group
+            ms.r[m] = make_rsrc(static_cast<const char*>(mods[m]) + (shared ? 0 : grp * a.mod_gs),
+                                xrow_bytes);
+        }
     }
     char* xr = static_cast<char*>(a.x) + row * a.x_rs;
     const rsrc_t rx = make_rsrc(xr, xrow_bytes);
@@ -166,35 +174,47 @@ __global__ void __launch_bounds__(kWaves * 64) adaln_kernel(AdalnArgs a) {
         shv.to_float(sh);
         scv.to_float(sc);
 #pragma unroll
-        for (int j = 0; j < VEC; ++j)
-            o[j] = __builtin_fmaf((v[i][j] - mean) * rstd, 1.0f + sc[j], sh[j]);
+        for (int j = 0; j < VEC; ++j) o[j] = (v[i][j] - mean) * rstd;
+        if constexpr (AFFINE) {
+            Vec<TX, VEC> gmv, btv;
+            ms.get(2, c, gmv);
+            ms.get(3, c, btv);
+            float gm[VEC], bt[VEC];
+            gmv.to_float(gm);
+            btv.to_float(bt);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) o[j] = __builtin_fmaf(o[j], gm[j], bt[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) o[j] = __builtin_fmaf(o[j], 1.0f + sc[j], sh[j]);
         Vec<TY, VEC> ov;
         ov.from_float(o);
         ov.template store_buf<kStoreStream>(ry, c * (VEC * sizeof(TY)));
     }
 }
 
-template <typename TX, typename TY, typename TH, int VEC, bool FUSED, int NV>
+template <typename TX, typename TY, typename TH, int VEC, bool FUSED, bool AFFINE, int NV>
 hipError_t launch_nv(const AdalnArgs& a, bool single_group, hipStream_t st) {
     const int64_t blocks = (a.rows + kWaves - 1) / kWaves;
-    const size_t lds = (size_t)(FUSED ? 3 : 2) * a.nvec * Vec<TX, VEC>::kQuads * 16;
+    const size_t lds = (size_t)(FUSED ? 3 : (AFFINE ? 4 : 2)) * a.nvec * Vec<TX, VEC>::kQuads * 16;
     // stage in LDS when there is one group and the staged vectors leave room for
     // several workgroups per CU
     if (single_group && lds <= 48 * 1024)
-        hipLaunchKernelGGL((adaln_kernel<TX, TY, TH, VEC, NV, FUSED, true>), dim3((unsigned)blocks),
-                           dim3(kWaves * 64), lds, st, a);
+        hipLaunchKernelGGL((adaln_kernel<TX, TY, TH, VEC, NV, FUSED, true, AFFINE>),
+                           dim3((unsigned)blocks), dim3(kWaves * 64), lds, st, a);
     else
-        hipLaunchKernelGGL((adaln_kernel<TX, TY, TH, VEC, NV, FUSED, false>),
+        hipLaunchKernelGGL((adaln_kernel<TX, TY, TH, VEC, NV, FUSED, false, AFFINE>),
                            dim3((unsigned)blocks), dim3(kWaves * 64), 0, st, a);
     return hipGetLastError();
 }
 
-template <typename TX, typename TY, typename TH, int VEC, bool FUSED>
+template <typename TX, typename TY, typename TH, int VEC, bool FUSED, bool AFFINE = false>
 h3f_status_t dispatch(const AdalnArgs& a, int max_nv, bool single_group, hipStream_t st) {
     const int need = (a.nvec + 63) / 64;
     hipError_t e = hipErrorInvalidValue;
 #define H3F_NV_CASE(N)                                                   \
-    else if (need <= N && N <= max_nv) e = launch_nv<TX, TY, TH, VEC, FUSED, N>(a, single_group, st);
+    else if (need <= N && N <= max_nv)                                   \
+        e = launch_nv<TX, TY, TH, VEC, FUSED, AFFINE, N>(a, single_group, st);
     if (false) {
     }
     H3F_NV_CASE(1) H3F_NV_CASE(2) H3F_NV_CASE(3) H3F_NV_CASE(4) H3F_NV_CASE(5) H3F_NV_CASE(6)
@@ -222,14 +242,16 @@ h3f_status_t check_mod(const void* p, int64_t groups, int64_t gs, int64_t hidden
 
 using namespace h3f;
 
-extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t y_row_stride,
-                                           const void* x, h3f_dtype_t x_dtype,
-                                           int64_t x_row_stride, const void* shift,
-                                           const void* scale, int64_t mod_group_stride,
-                                           int64_t rows_per_group, int64_t rows, int64_t hidden,
-                                           float eps, void* stream) {
-    if (rows == 0) return H3F_OK;
-    if (!y || !x || !shift || !scale) return H3F_ERR_NULL_POINTER;
+namespace {
+
+// Shared by the plain and the LayerNorm-affine entry points (gamma, beta NULL
+// for the plain one).
+h3f_status_t adaln_entry(void* y, h3f_dtype_t y_dtype, int64_t y_row_stride, const void* x,
+                         h3f_dtype_t x_dtype, int64_t x_row_stride, const void* gamma,
+                         const void* beta, const void* shift, const void* scale,
+                         int64_t mod_group_stride, int64_t rows_per_group, int64_t rows,
+                         int64_t hidden, float eps, void* stream) {
+    const bool affine = gamma != nullptr;
     if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return H3F_ERR_BAD_DTYPE;
     if (x_dtype == H3F_BF16 && y_dtype == H3F_F32) return H3F_ERR_BAD_DTYPE;
     if (rows < 0 || hidden <= 0 || rows_per_group < 1) return H3F_ERR_BAD_SHAPE;
@@ -237,6 +259,7 @@ extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t
     if (hidden % V) return H3F_ERR_BAD_SHAPE;
     if (hidden > max_hidden(x_dtype) || rows > 0x7fffffff) return H3F_ERR_UNSUPPORTED;
     if (!aligned16(y) || !aligned16(x)) return H3F_ERR_MISALIGNED;
+    if (affine && (!aligned16(gamma) || !aligned16(beta))) return H3F_ERR_MISALIGNED;
     const int64_t groups = groups_for(rows, rows_per_group);
     h3f_status_t s;
     if ((s = check_mod(shift, groups, mod_group_stride, hidden, V)) != H3F_OK) return s;
@@ -254,6 +277,9 @@ extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t
         return H3F_ERR_BAD_STRIDE;
     if (!alias_ok(ry, rx, x_dtype == y_dtype) || !disjoint(ry, rsh) || !disjoint(ry, rsc))
         return H3F_ERR_ALIASING;
+    if (affine && (!disjoint(ry, region2d(gamma, 1, 0, hidden, ex)) ||
+                   !disjoint(ry, region2d(beta, 1, 0, hidden, ex))))
+        return H3F_ERR_ALIASING;
 
     AdalnArgs a{};
     a.y = y;
@@ -262,6 +288,8 @@ extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t
     a.x_rs = (rows > 1 ? x_row_stride : hidden) * ex;
     a.shift = shift;
     a.scale = scale;
+    a.gamma = gamma;
+    a.beta = beta;
     a.mod_gs = (groups > 1 ? mod_group_stride : 0) * ex;
     a.div_group = make_fastdiv((uint32_t)(rows_per_group > rows ? rows : rows_per_group));
     a.rows = rows;
@@ -272,11 +300,43 @@ extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int mnv = max_nv_for(x_dtype, V);
     const bool one = groups == 1;
+    if (affine) {
+        if (x_dtype == H3F_F32 && y_dtype == H3F_F32)
+            return dispatch<float, float, float, 4, false, true>(a, mnv, one, st);
+        if (x_dtype == H3F_BF16)
+            return dispatch<__bf16, __bf16, __bf16, 8, false, true>(a, mnv, one, st);
+        return dispatch<float, __bf16, float, 4, false, true>(a, mnv, one, st);
+    }
     if (x_dtype == H3F_F32 && y_dtype == H3F_F32)
         return dispatch<float, float, float, 4, false>(a, mnv, one, st);
     if (x_dtype == H3F_BF16)
         return dispatch<__bf16, __bf16, __bf16, 8, false>(a, mnv, one, st);
     return dispatch<float, __bf16, float, 4, false>(a, mnv, one, st);
+}
+
+}  // namespace
+
+extern "C" h3f_status_t h3f_adaln_modulate(void* y, h3f_dtype_t y_dtype, int64_t y_row_stride,
+                                           const void* x, h3f_dtype_t x_dtype,
+                                           int64_t x_row_stride, const void* shift,
+                                           const void* scale, int64_t mod_group_stride,
+                                           int64_t rows_per_group, int64_t rows, int64_t hidden,
+                                           float eps, void* stream) {
+    if (rows == 0) return H3F_OK;
+    if (!y || !x || !shift || !scale) return H3F_ERR_NULL_POINTER;
+    return adaln_entry(y, y_dtype, y_row_stride, x, x_dtype, x_row_stride, nullptr, nullptr,
+                       shift, scale, mod_group_stride, rows_per_group, rows, hidden, eps, stream);
+}
+
+extern "C" h3f_status_t h3f_adaln_affine_modulate(
+    void* y, h3f_dtype_t y_dtype, int64_t y_row_stride, const void* x, h3f_dtype_t x_dtype,
+    int64_t x_row_stride, const void* gamma, const void* beta, const void* shift,
+    const void* scale, int64_t mod_group_stride, int64_t rows_per_group, int64_t rows,
+    int64_t hidden, float eps, void* stream) {
+    if (rows == 0) return H3F_OK;
+    if (!y || !x || !gamma || !beta || !shift || !scale) return H3F_ERR_NULL_POINTER;
+    return adaln_entry(y, y_dtype, y_row_stride, x, x_dtype, x_row_stride, gamma, beta, shift,
+                       scale, mod_group_stride, rows_per_group, rows, hidden, eps, stream);
 }
 
 extern "C" h3f_status_t h3f_gated_residual_adaln(
