@@ -14,7 +14,14 @@
 // its group's vectors through the cache hierarchy (L1/L2, not HBM).
 // Measured on MI355X: one row per wavefront, no grid-stride reuse, is the
 // fastest organisation (multi-wavefront rows pay more in barriers than they
-// gain in finer-grained streaming).
+// gain in finer-grained streaming).  The order in which a wavefront issues its
+// row loads matters by ~3%: they go out strictly in address order (scheduling
+// barriers keep the compiler from interleaving them).  The plain kernel stages
+// the modulation first and then issues a bf16 row at raised wave priority, so
+// a wavefront's loads leave back to back; the fused kernel, which has twice the
+// loads per row, instead issues x before the staging so that the row's latency
+// overlaps the staging and the barrier.  Each choice was the faster of the two
+// for its kernel (about 5% each at hidden 5120).
 #include <hip/hip_runtime.h>
 
 #include "h3f_device.hpp"
@@ -68,6 +75,18 @@ struct ModSource {
 
 extern __shared__ u32x4 adaln_lds[];
 
+// Copies group 0's NMOD modulation vectors (nvec chunks of Q quads each) into
+// LDS; every thread of the workgroup must call it (it ends with a barrier).
+template <int NMOD, int Q, int NTHREADS>
+__device__ __forceinline__ void stage_mods(const void* const* mods, int32_t nvec) {
+    const int per = nvec * Q;
+    for (int i = threadIdx.x; i < NMOD * per; i += NTHREADS) {
+        const int which = i / per;
+        adaln_lds[i] = ld16(static_cast<const char*>(mods[which]) + (size_t)(i - which * per) * 16);
+    }
+    __syncthreads();
+}
+
 // Vectors read per row: shift, scale, then gate (FUSED) or gamma, beta (AFFINE).
 template <typename TX, typename TY, typename TH, int VEC, int NV, bool FUSED, bool LDSMOD,
           bool AFFINE>
@@ -82,18 +101,16 @@ __global__ void __launch_bounds__(kWaves * 64) adaln_kernel(AdalnArgs a) {
     ModSource<TX, VEC, LDSMOD> ms;
     ms.nvec = a.nvec;
     ms.lds = adaln_lds;
-    if constexpr (LDSMOD) {
-        // stage group 0's vectors: NMOD x nvec chunks of Q quads
-        const int per = a.nvec * Q;
-        for (int i = threadIdx.x; i < NMOD * per; i += kWaves * 64) {
-            const int which = i / per;
-            adaln_lds[i] = ld16(static_cast<const char*>(mods[which]) + (size_t)(i - which * per) * 16);
-        }
-        __syncthreads();
-    }
+    // the fused kernel stages after issuing its x loads (see the file comment)
+    constexpr bool kStageLate = LDSMOD && FUSED;
+    if constexpr (LDSMOD && !kStageLate) stage_mods<NMOD, Q, kWaves * 64>(mods, a.nvec);
 
-    const int64_t row = uniform64((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6));
-    if (row >= a.rows) return;
+    const int64_t row_raw = uniform64((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6));
+    if constexpr (!kStageLate)
+        if (row_raw >= a.rows) return;
+    // with late staging a spare wavefront of the last workgroup must still reach
+    // the barrier: it loads the last row again and returns before any store
+    const int64_t row = row_raw < a.rows ? row_raw : a.rows - 1;
     const uint32_t grp = fdiv((uint32_t)row, a.div_group);
     if constexpr (!LDSMOD) {
 #pragma unroll
@@ -109,11 +126,21 @@ __global__ void __launch_bounds__(kWaves * 64) adaln_kernel(AdalnArgs a) {
     bool valid[NV];
     {
         Vec<TX, VEC> xv[NV];
+        // raised priority pays for bf16 rows (10 loads at hidden 5120) and costs ~2%
+        // for fp32 rows (20 loads), which keep the default
+        constexpr bool kPrio = !FUSED && sizeof(TX) == 2;
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int c = i * 64 + lane;
             valid[i] = c < a.nvec;
             xv[i].template load_buf<kLoadStream>(rx, (uint32_t)c * (VEC * sizeof(TX)));
+            __builtin_amdgcn_sched_barrier(0);  // keep the loads in address order
+        }
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+        if constexpr (kStageLate) {
+            stage_mods<NMOD, Q, kWaves * 64>(mods, a.nvec);
+            if (row_raw >= a.rows) return;
         }
         if constexpr (FUSED) {
             const rsrc_t rh = make_rsrc(static_cast<const char*>(a.h) + row * a.h_rs,
