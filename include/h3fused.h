@@ -32,7 +32,9 @@
  *   - Modulation vectors (shift, scale, gate) are [groups, hidden] rows: token
  *     row r uses group g = r / rows_per_group (rows_per_group = rows gives one
  *     vector for the whole call; 1 gives per-token modulation).
- *   - rows == 0 is a no-op that returns H3F_OK before any other check.
+ *   - For the per-token operators rows == 0 is a no-op that returns H3F_OK
+ *     before any other check.  The residual difference and the router reject
+ *     it (they have no result for an empty tensor; see there).
  *   - Validation is synchronous and happens before any launch; a bad argument
  *     returns an error code and launches nothing.  No call aborts or throws.
  *   - Aliasing: an output may be exactly the same tensor as an input (same
@@ -275,9 +277,9 @@ h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cur_row_strid
  * h3f_qk_rmsnorm_rope3d; strides multiples of 8, pointers 16-byte aligned).
  * kv_blocks: device int32 [heads, n_blocks, keep], dense, 4-byte aligned.
  * scores: device fp32 [heads, n_blocks, n_blocks], dense, 16-byte aligned,
- * written on routed steps only (required on every step).  workspace: device scratch of at least
- * workspace_bytes (16-byte aligned, no initialisation needed; calls sharing
- * one must be ordered on one stream).  Outputs and workspace must not overlap
+ * written on routed steps only (but required on every step).  workspace:
+ * device scratch of at least workspace_bytes (16-byte aligned, no
+ * initialisation needed; calls sharing one must be ordered on one stream).  Outputs and workspace must not overlap
  * each other or q, k.  On a dense step (step < H3F_SUBBLOCK_FIRST_STEP) the
  * call only writes kv_blocks[h,i,:] = 0..n_blocks-1 and reads neither q nor k.
  * Errors: H3F_ERR_UNSUPPORTED for a dtype other than bf16, head_dim != 128,

@@ -382,6 +382,15 @@ def test_qk_other_head_dims():
     _qk_case(dict(TINY, Dh=32, split=(8, 8, 16), heads=2), "f32", 30)
 
 
+def test_qk_head_dim_limits():
+    # the largest heads the kernel takes (one head per wavefront: 64 lanes x 8 bf16)
+    # and the smallest fp32 head (head_dim / 4 = 4 lanes per head, 16 heads per wavefront)
+    _qk_case(dict(TINY, Dh=512, split=(128, 192, 192), heads=3), "bf16", 37, offset=11)
+    _qk_case(dict(TINY, Dh=512, split=(128, 192, 192), heads=2), "bf16", 21, offset=90,
+             pairing=h3.H3F_ROPE_HALF_SPLIT)
+    _qk_case(dict(TINY, Dh=16, split=(4, 4, 8), heads=7), "f32", 45, offset=60)
+
+
 # ------------------------------------------------------------------------------------
 # full 5 s shapes (the measured workload), sampled rows
 # ------------------------------------------------------------------------------------
