@@ -253,7 +253,11 @@ def test_adaln_constant_rows_give_shift():
 
 FUSED_CASES = [(112, 256, "f32", "f32", "f32"), (1001, 5120, "bf16", "bf16", "bf16"),
                (513, 5120, "f32", "bf16", "bf16"), (200, 3072, "f32", "f32", "bf16"),
-               (64, 4096, "f32", "bf16", "f32")]
+               (64, 4096, "f32", "bf16", "f32"),
+               # widest rows, and one row (the other wavefronts of its workgroup
+               # only take part in the modulation staging)
+               (65, 16384, "bf16", "bf16", "bf16"), (33, 8192, "f32", "f32", "f32"),
+               (1, 5120, "bf16", "bf16", "bf16"), (3, 5120, "f32", "bf16", "bf16")]
 
 
 @pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "x".join(map(str, c)))
@@ -462,6 +466,26 @@ def test_guard_bands_untouched():
     h3.h3f_swiglu(y, gu)
     b = to_np(buf.float())
     assert np.all(b[:pad] == -7.0) and np.all(b[pad + rows * D:] == -7.0)
+
+
+@pytest.mark.parametrize("rows", [1, 2, 5])
+def test_fused_guard_rows_untouched(rows):
+    # x and y sit inside larger buffers whose later rows the call must not touch:
+    # the spare wavefronts of the last workgroup load the last row again for the
+    # modulation staging but store nothing
+    D, extra = 5120, 7
+    xb = torch.full((rows + extra, D), -3.0, dtype=torch.bfloat16, device=DEV)
+    yb = torch.full((rows + extra, D), -5.0, dtype=torch.bfloat16, device=DEV)
+    h3gen.fill_device(xb[:rows], "x")
+    h = dev_tensor("h", rows, D, "bf16")
+    gt, sh, sc = (dev_tensor(n, 1, D, "bf16") for n in ("gate", "shift", "scale"))
+    h3.h3f_gated_residual_adaln(xb[:rows], h, gt, sh, sc, yb[:rows])
+    assert torch.all(xb[rows:] == -3.0) and torch.all(yb[rows:] == -5.0)
+    rx, ry = oracle.gated_residual_adaln(
+        host("x", rows, D, "bf16"), host("h", rows, D, "bf16"),
+        *(host(n, 1, D, "bf16") for n in ("gate", "shift", "scale")), y_dtype=np.uint16)
+    assert_close(to_np(xb[:rows]), rx, kind("bf16"), "fused x")
+    assert_close(to_np(yb[:rows]), ry, kind("bf16"), "fused y")
 
 
 def test_zero_rows_is_noop_and_errors_raise():
