@@ -407,7 +407,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32",  # arithmetic; every kernel computes in fp32 on bf16 / fp32 storage
+        "storage_dtype": ("fp32 residual stream, bf16 activations" if chain else "bf16"),
         "data": "synthetic (seeded counter-based generator, N(0,1)-like activations)",
         "config": config,
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
