@@ -178,7 +178,25 @@ def make_step(h3, t, rope, fused):
 
 
 def cpu_baseline(c, rows, x_bytes, min_seconds=10.0, seed=0):
-    """Time the oracle on `rows` rows of the same workload (one block's six calls)."""
+    """Time the oracle on `rows` rows of the same workload (one block's six calls),
+    on all the host threads it uses, and again on one thread over a sixteenth of
+    the sample."""
+    import oracle
+
+    full = _time_oracle(c, rows, x_bytes, min_seconds, seed)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        one = _time_oracle(c, max(1, rows // 16), x_bytes, min_seconds / 2, seed)
+    finally:
+        oracle.set_num_threads(threads)
+    full["single_thread"] = {"value": one["value"], "unit": "GB/s", "cores": 1,
+                             "seconds": one["seconds"], "steps": one["steps"],
+                             "sample": one["sample"]}
+    return full
+
+
+def _time_oracle(c, rows, x_bytes, min_seconds, seed):
     import numpy as np
 
     import h3gen
@@ -316,10 +334,13 @@ def main():
 
     per_op_ms = {}
     per_op_n = {}
+    per_op_all = {}
     for s in range(K):
         for i, (name, _) in enumerate(step):
-            per_op_ms[name] = per_op_ms.get(name, 0.0) + launch_ms(s, i)
+            ms = launch_ms(s, i)
+            per_op_ms[name] = per_op_ms.get(name, 0.0) + ms
             per_op_n[name] = per_op_n.get(name, 0) + 1
+            per_op_all.setdefault(name, []).append(ms)
     if flush is None:
         ms_per_step = start.elapsed_time(stop) / K
     else:  # the flushes between launches are not part of a step
@@ -330,7 +351,10 @@ def main():
     for name in per_op_ms:
         avg = per_op_ms[name] / per_op_n[name]
         b = op_bytes(name, N, c, x_bytes)
-        per_op[name] = {"avg_ms": round(avg, 4), "bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+        ts = sorted(per_op_all[name])
+        per_op[name] = {"avg_ms": round(avg, 4), "median_ms": round(ts[len(ts) // 2], 4),
+                        "min_ms": round(ts[0], 4), "launches": len(ts),
+                        "bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1),
                         "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                         "frac_of_copy_ceiling": round(b / (avg * 1e-3) / 1e9 / copy_gbps, 4)}
 
