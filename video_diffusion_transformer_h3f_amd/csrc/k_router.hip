@@ -266,13 +266,21 @@ __device__ __forceinline__ uint32_t xcd_linear(uint32_t w, uint32_t n) {
 }
 
 // Strip form: a workgroup keeps one 64-row tile of Qm in registers and walks
-// a run of kScoreRun 64-column tiles of Km, loading the next tile's operands
-// while the matrix cores work on the current one (two register sets,
-// alternating; the run is fully unrolled so the loads in flight are tracked
-// exactly).  The MFMA is fed Km as its first operand and Qm as its second, so
-// it produces the transposed tile: lane (ri, g) holds scores[i0 + ri][j0 +
-// 4 g .. 4 g + 3], one 16-byte store per 16 x 16 tile.  Column tiles past the
-// last one read zeros and store nothing.
+// a run of kScoreRun 64-column tiles of Km.  Each Km tile (64 rows x 128
+// floats) is gathered into LDS once per workgroup with 16-byte buffer-to-LDS
+// loads, already in the order the matrix instructions take it: 1 KiB
+// fragments (rows 16 R .. 16 R + 15, columns 16 v .. 16 v + 15) in which lane
+// ri + 16 g holds row 16 R + ri, columns 16 v + 4 g .. + 3.  Every wavefront
+// then reads its operands with linear, conflict-free 16-byte LDS reads, and
+// the two wavefronts that share key columns no longer load them twice.  Two
+// LDS buffers alternate, the next tile's gather in flight during the current
+// tile's matrix instructions (one barrier per tile).  The MFMA is fed Km as
+// its first operand and Qm as its second, so it produces the transposed
+// tile: lane (ri, g) holds scores[i0 + ri][j0 + 4 g .. 4 g + 3], one 16-byte
+// store per 16 x 16 tile.  Rows and column tiles past the last block read
+// zeros and store nothing.  Measured at the 5 s shape: 125 us with the
+// operands pipelined through registers instead, 115 us this way; runs of 4
+// and 16 tiles were slower than 8.
 #ifndef H3F_SCORE_RUN
 #define H3F_SCORE_RUN 8
 #endif
@@ -334,8 +342,20 @@ __device__ __forceinline__ void store_tile32_t(rsrc_t r, uint32_t nb, uint32_t i
     }
 }
 
+constexpr int kTileFrags = (kTile / 16) * 8;  // 1 KiB fragments per 64-row key tile
+
+// vmcnt(n stores per tile): this wavefront's gather of the next tile is
+// complete while the current tile's stores, issued after it, may still be in
+// flight.
+template <int SB>
+__device__ __forceinline__ void wait_own_gather() {
+    constexpr int n = SB == 16 ? 4 : (SB == 8 ? 8 : 16);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
 template <int SB>
 __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
+    __shared__ u32x4 kbuf[2][kTileFrags * 64];
     const uint32_t runs = (a.tiles + kScoreRun - 1) / kScoreRun;
     const uint32_t per_head = a.tiles * runs;
     const uint32_t w = xcd_linear(blockIdx.x, (uint32_t)a.heads * per_head);
@@ -344,34 +364,57 @@ __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
     const uint32_t ti = rem / runs;
     const uint32_t run = rem - ti * runs;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ri = lane & 15;
     const int g = lane >> 4;
     const uint32_t i0 = ti * kTile + (wave >> 1) * kWaveTile;
-    const uint32_t jbase = run * kScoreRun * kTile + (wave & 1) * kWaveTile;
+    const uint32_t jrun = run * kScoreRun * kTile;
+    const int rj = (wave & 1) * 2;  // first 16-row group of this wavefront's key rows
 
     const uint32_t mat_bytes = a.nb * kHeadDim * 4u;
     const rsrc_t rq = make_rsrc(a.pooled + (size_t)h * a.nb * kHeadDim, mat_bytes);
     const rsrc_t rk = make_rsrc(a.pooled + ((size_t)a.heads + h) * a.nb * kHeadDim, mat_bytes);
     const rsrc_t ro = make_rsrc(a.scores + (size_t)h * a.nb * a.nb, a.nb * a.nb * 4u);
 
-    float A[2][32], B[2][2][32];
+    // wavefront w gathers fragments 8 w .. 8 w + 7 of key tile t into buffer b;
+    // lane ri + 16 g of fragment f takes 16 bytes of row 16 (f / 8) + ri at
+    // column 16 (f mod 8) + 4 g (rows past nb read 0)
+    auto gather = [&](uint32_t t, int b) {
+#pragma unroll
+        for (int f8 = 0; f8 < 8; ++f8) {
+            const int f = wave * 8 + f8;
+            const uint32_t row = jrun + t * kTile + 16u * (uint32_t)(f >> 3) + (uint32_t)ri;
+            const uint32_t off = row * (kHeadDim * 4u) + 64u * (uint32_t)(f & 7) + 16u * (uint32_t)g;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, (__attribute__((address_space(3))) void*)&kbuf[b][f * 64], 16, off, 0, 0,
+                kLoadReuse);
+        }
+    };
+
+    float A[2][32], B[2][32];
 #pragma unroll
     for (int m = 0; m < 2; ++m) load_row32(A[m], rq, i0 + 16 * m + ri, g);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) load_row32(B[0][n], rk, jbase + 16 * n + ri, g);
+    gather(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     f32x4 acc[2][2];
 #pragma unroll
     for (uint32_t t = 0; t < kScoreRun; ++t) {
-        if (t + 1 < kScoreRun) {
+        if (t > 0) wait_own_gather<SB>();
+        __syncthreads();  // every gather of tile t is complete; buffer (t + 1) & 1 is free
 #pragma unroll
-            for (int n = 0; n < 2; ++n)
-                load_row32(B[(t + 1) & 1][n], rk, jbase + (t + 1) * kTile + 16 * n + ri, g);
-        }
-        // keep the next tile's loads ahead of this tile's matrix instructions
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const u32x4 x = kbuf[t & 1][((rj + n) * 8 + v) * 64 + lane];
+                B[n][4 * v + 0] = __uint_as_float(x[0]);
+                B[n][4 * v + 1] = __uint_as_float(x[1]);
+                B[n][4 * v + 2] = __uint_as_float(x[2]);
+                B[n][4 * v + 3] = __uint_as_float(x[3]);
+            }
+        if (t + 1 < kScoreRun) gather(t + 1, (t + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_tile32_t(acc, A, B[t & 1]);
-        store_tile32_t<SB>(ro, a.nb, i0, jbase + t * kTile, ri, g, acc);
+        mfma_tile32_t(acc, A, B);
+        store_tile32_t<SB>(ro, a.nb, i0, jrun + t * kTile + (wave & 1) * kWaveTile, ri, g, acc);
     }
 }
 
