@@ -395,6 +395,31 @@ def main():
             "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "block": blk, "sparsity": sp, "n_blocks": nb, "keep": keep,
             "score_flops": 2 * c["heads"] * nb * nb * c["Dh"]}
+
+        # A routed step with the router's pooling fused into the QK operator: the
+        # QK call that also writes the block means, then the route from them.
+        def qk_pool():
+            h3.h3f_qk_rmsnorm_rope3d_pool(t["q_out"], t["k_out"], t["q"], t["k"], t["q_weight"],
+                                          t["k_weight"], rope, blk, ws)
+
+        def route_pooled():
+            h3.h3f_subblock_route_pooled(kv, sc, N, c["heads"], blk, sp, 10, ws)
+
+        for _ in range(3):
+            qk_pool()
+            route_pooled()
+        torch.cuda.synchronize()
+        a_qp = time_calls(qk_pool, K)
+        a_rp = time_calls(route_pooled, K)
+        b_qp = op_bytes("qk", N, c, x_bytes) + 2 * c["heads"] * nb * c["Dh"] * 4
+        b_rp = c["heads"] * nb * nb * 4 + c["heads"] * nb * keep * 4 + 2 * c["heads"] * nb * c["Dh"] * 4
+        extra_ops["qk_rmsnorm_rope3d_pool"] = {
+            "avg_ms": round(a_qp, 4), "bytes": b_qp, "GBps": round(b_qp / (a_qp * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(b_qp / (a_qp * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        extra_ops["subblock_route_pooled"] = {
+            "avg_ms": round(a_rp, 4), "bytes": b_rp, "GBps": round(b_rp / (a_rp * 1e-3) / 1e9, 1)}
+        extra_ops["routed_qk_step_ms"] = {
+            "separate": round(per_op["qk"]["avg_ms"] + avg, 4), "fused": round(a_qp + a_rp, 4)}
         del kv, sc, ws
 
     dom = "swiglu"

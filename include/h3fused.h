@@ -304,6 +304,49 @@ h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores,
                                 void* stream);
 
 /*
+ * QK RMSNorm + 3D RoPE with the router's block pooling fused in.  Writes
+ * q_out and k_out exactly as h3f_qk_rmsnorm_rope3d does (bit-identical), and
+ * in the same pass the router's block means of the values as stored --
+ * qm[h,b,:], km[h,b,:] over token blocks of `block` rows, as described for
+ * h3f_subblock_route -- into `workspace`, so that a routed step needs no
+ * second read of q_out and k_out (h3f_subblock_route_pooled then finishes the
+ * route from the workspace).  This keeps the tensors resident in the producing
+ * kernel instead of re-reading them, the fusion the report page credits with
+ * its gains (section "Só com três camadas…").
+ * Arguments as h3f_qk_rmsnorm_rope3d, plus block and the workspace of
+ * h3f_subblock_plan (same rows, heads, head_dim, block); the router's
+ * preconditions apply (bf16, head_dim 128, rows >= 4096, n_blocks <= 8192,
+ * heads <= 4096; H3F_ERR_UNSUPPORTED otherwise, and rows == 0 is rejected).
+ * Errors: as h3f_qk_rmsnorm_rope3d; H3F_ERR_WORKSPACE for a missing,
+ * misaligned or short workspace; H3F_ERR_ALIASING if it overlaps a tensor.
+ * The block sums run in token order in fp32, so the means can differ from the
+ * separate route's in the last bits.
+ */
+h3f_status_t h3f_qk_rmsnorm_rope3d_pool(void* q_out, int64_t q_out_row_stride,
+                                        int64_t q_out_head_stride, void* k_out,
+                                        int64_t k_out_row_stride, int64_t k_out_head_stride,
+                                        const void* q, int64_t q_row_stride,
+                                        int64_t q_head_stride, const void* k,
+                                        int64_t k_row_stride, int64_t k_head_stride,
+                                        const void* q_weight, const void* k_weight,
+                                        h3f_dtype_t dtype, int64_t rows, int32_t heads,
+                                        int32_t head_dim, float eps, const h3f_rope3d_t* rope,
+                                        int32_t block, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
+ * The router's score and selection from block means already in `workspace`
+ * (written by h3f_qk_rmsnorm_rope3d_pool with the same rows, heads, head_dim
+ * and block, earlier on the same stream).  Outputs, sizes, step rule, errors
+ * and determinism as h3f_subblock_route; on a dense step the workspace is
+ * neither needed nor read.
+ */
+h3f_status_t h3f_subblock_route_pooled(int32_t* kv_blocks, float* scores, int64_t rows,
+                                       int32_t heads, int32_t head_dim, int32_t block,
+                                       double sparsity, int32_t step, const void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * Streaming copy (measurement helper, not an operator): dst[0:bytes) =
  * src[0:bytes) with 16-byte vector loads and stores.  Used to measure the
  * achievable HBM bandwidth and to calibrate hardware byte counters.  bytes

@@ -317,6 +317,48 @@ def test_subblock_route_validation():
     assert route(kv=P(0x40000000 + 1024)) == ALIAS  # kv_blocks inside k
 
 
+def test_qk_pool_validation():
+    # the fused QK + router pooling: QK's own checks, then the router's
+    # preconditions and its workspace (4096 tokens x 8 heads, 32 blocks of 128:
+    # 2 x 8 x 32 x 128 x 4 = 256 KiB of block means)
+    def qkp(qo=A(0), ko=A(1), q=A(2), k=A(3), qw=A(4), kw=A(5), dt=BF16, rows=4096, heads=8,
+            hd=128, r=None, block=128, ws=A(6), wsb=1 << 18, qrs=1024):
+        r = rope() if r is None else r
+        return L.h3f_qk_rmsnorm_rope3d_pool(qo, 1024, 128, ko, 1024, 128, q, qrs, 128, k, 1024,
+                                            128, qw, kw, dt, rows, heads, hd, ctypes.c_float(1e-6),
+                                            ctypes.byref(r), block, ws, wsb, None)
+
+    assert qkp(q=None) == NULLP
+    assert qkp(rows=4095) == UNSUP            # the router's minimum sequence
+    assert qkp(rows=0) == UNSUP               # not a no-op here
+    assert qkp(hd=64) == UNSUP
+    assert qkp(block=0) == SHAPE
+    assert qkp(dt=F32) == UNSUP               # router input is bf16 only
+    assert qkp(dt=3) == DTYPE
+    assert qkp(r=rope(d_t=40)) == SHAPE         # 40 + 48 + 48 != head_dim
+    assert qkp(ws=None) == WORKSPACE
+    assert qkp(wsb=(1 << 18) - 16) == WORKSPACE
+    assert qkp(ws=P(0x70000008)) == WORKSPACE
+    assert qkp(ws=P(0x10000000 + 4096)) == ALIAS   # inside q_out
+    assert qkp(qrs=1020) == STRIDE
+
+
+def test_route_pooled_validation():
+    def rp(kv=A(0), sc=A(1), rows=4096, heads=8, hd=128, block=128, sp=0.8, step=10, ws=A(2),
+           wsb=1 << 18):
+        return L.h3f_subblock_route_pooled(kv, sc, rows, heads, hd, block, sp, step, ws, wsb, None)
+
+    assert rp(kv=None) == NULLP
+    assert rp(sc=None) == NULLP
+    assert rp(rows=100) == UNSUP
+    assert rp(sp=1.0) == BADVAL
+    assert rp(step=0) == BADVAL
+    assert rp(sc=P(0x20000004)) == MISAL
+    assert rp(ws=None) == WORKSPACE
+    assert rp(wsb=(1 << 18) - 1) == WORKSPACE
+    assert rp(ws=P(0x20000000 + 256)) == ALIAS     # workspace inside the scores
+
+
 def test_subblock_binding_checks_shapes_before_the_library():
     import torch
 

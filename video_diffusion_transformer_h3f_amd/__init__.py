@@ -35,6 +35,7 @@ EXPORTS = [
     "h3f_gated_residual", "h3f_swiglu", "h3f_qk_rmsnorm_rope3d", "h3f_gated_residual_adaln",
     "h3f_stream_copy", "h3f_residual_l1_workspace_bytes", "h3f_residual_l1",
     "h3f_subblock_plan", "h3f_subblock_route", "h3f_adaln_affine_modulate",
+    "h3f_qk_rmsnorm_rope3d_pool", "h3f_subblock_route_pooled",
 ]
 
 
@@ -93,6 +94,12 @@ def lib():
                                         ctypes.POINTER(ctypes.c_size_t)]
         L.h3f_subblock_route.argtypes = [p, p, p, i64, i64, p, i64, i64, st, i64, i32, i32, i32,
                                          ctypes.c_double, i32, p, ctypes.c_size_t, p]
+        L.h3f_qk_rmsnorm_rope3d_pool.argtypes = [p, i64, i64, p, i64, i64, p, i64, i64, p, i64,
+                                                 i64, p, p, st, i64, i32, i32, f,
+                                                 ctypes.POINTER(Rope3D), i32, p, ctypes.c_size_t,
+                                                 p]
+        L.h3f_subblock_route_pooled.argtypes = [p, p, i64, i32, i32, i32, ctypes.c_double, i32, p,
+                                                ctypes.c_size_t, p]
         _lib = L
     return _lib
 
@@ -280,6 +287,58 @@ def _heads3d(t, name):
     if t.dim() != 3 or t.stride(2) != 1:
         raise ValueError(f"{name}: expected [rows, heads, head_dim] with unit inner stride")
     return t.shape, t.stride(0), t.stride(1)
+
+
+def _qk_args(q_out, k_out, q, k, q_weight, k_weight):
+    shp, qrs, qhs = _heads3d(q, "q")
+    kshp, krs, khs = _heads3d(k, "k")
+    qoshp, qors, qohs = _heads3d(q_out, "q_out")
+    koshp, kors, kohs = _heads3d(k_out, "k_out")
+    if not (shp == kshp == qoshp == koshp):
+        raise ValueError("q, k, q_out, k_out shapes differ")
+    rows, heads, head_dim = shp
+    for w, n in ((q_weight, "q_weight"), (k_weight, "k_weight")):
+        if w.numel() != head_dim or not w.is_contiguous():
+            raise ValueError(f"{n}: expected a contiguous [head_dim] tensor")
+    dt = _dtype(q)
+    for t in (k, q_out, k_out, q_weight, k_weight):
+        if _dtype(t) != dt:
+            raise TypeError("all qk tensors must share one dtype")
+    return (_ptr(q_out), qors, qohs, _ptr(k_out), kors, kohs, _ptr(q), qrs, qhs, _ptr(k), krs,
+            khs, _ptr(q_weight), _ptr(k_weight), dt, rows, heads, head_dim)
+
+
+def h3f_qk_rmsnorm_rope3d_pool(q_out, k_out, q, k, q_weight, k_weight, rope: Rope3D,
+                               block: int, workspace, eps: float = 1e-6, stream=None):
+    """h3f_qk_rmsnorm_rope3d that also writes the router's block means of q_out and
+    k_out into `workspace` (uint8 GPU tensor of at least the bytes h3f_subblock_plan
+    gives for the same rows, heads, head_dim and block)."""
+    dev = _dev(q_out, k_out, q, k, q_weight, k_weight, workspace)
+    args = _qk_args(q_out, k_out, q, k, q_weight, k_weight)
+    _check("h3f_qk_rmsnorm_rope3d_pool", lib().h3f_qk_rmsnorm_rope3d_pool(
+        *args, eps, ctypes.byref(rope), block, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev, stream)))
+    return q_out, k_out
+
+
+def h3f_subblock_route_pooled(kv_blocks, scores, rows: int, heads: int, block: int,
+                              sparsity: float, step: int, workspace, stream=None):
+    """Router score + selection from the block means h3f_qk_rmsnorm_rope3d_pool wrote
+    into `workspace`; kv_blocks / scores as for h3f_subblock_route."""
+    import torch
+
+    dev = _dev(kv_blocks, scores, workspace)
+    if kv_blocks.dtype != torch.int32 or scores.dtype != torch.float32:
+        raise TypeError("kv_blocks must be int32 and scores float32")
+    if not (kv_blocks.is_contiguous() and scores.is_contiguous()):
+        raise ValueError("kv_blocks and scores must be contiguous")
+    nb, keep, _ = h3f_subblock_plan(rows, heads, 128, block, sparsity, step)
+    if tuple(kv_blocks.shape) != (heads, nb, keep) or tuple(scores.shape) != (heads, nb, nb):
+        raise ValueError(f"kv_blocks must be [{heads}, {nb}, {keep}] and scores [{heads}, {nb}, {nb}]")
+    _check("h3f_subblock_route_pooled", lib().h3f_subblock_route_pooled(
+        _ptr(kv_blocks), _ptr(scores), rows, heads, 128, block, float(sparsity), step,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev, stream)))
+    return kv_blocks, scores
 
 
 def h3f_qk_rmsnorm_rope3d(q_out, k_out, q, k, q_weight, k_weight, rope: Rope3D,

@@ -27,6 +27,11 @@ namespace {
 
 constexpr int kMaxPairs = 256;
 
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+// A buffer offset past any resource: the store is dropped.
+constexpr uint32_t kDroppedOffset = 0xFFFFFFF0u;
+
 // Token grid: row r (of the whole call) is token p = (offset + r) mod period;
 // offset is reduced modulo period on the host and offset + rows < 2^31.
 struct GridArgs {
@@ -85,11 +90,108 @@ __device__ __forceinline__ void token_position(const GridArgs& g, int64_t row, i
     }
 }
 
+// What a lane needs of the frequency table, read once per workgroup (the table
+// lives in the kernel arguments; indexing it by lane is a memory load, which
+// inside a token loop would also wait for every load in flight).
+template <int VEC, int LPH, bool HALF>
+struct LaneFreq {
+    static constexpr int NA = HALF ? VEC : VEC / 2;  // rotation pairs touched by a lane
+    static constexpr bool kShared = !HALF && LPH * VEC / 2 <= 64;
+    float f[kShared ? 1 : NA];  // shared: pair `lane`; otherwise the lane's own pairs
+    int ax;                     // axis (0 t, 1 h, 2 w) of those pairs
+};
+
+template <int VEC, int LPH, bool HALF>
+__device__ __forceinline__ LaneFreq<VEC, LPH, HALF> lane_freq(const QKArgs& a, int lane, int e0) {
+    using LF = LaneFreq<VEC, LPH, HALF>;
+    LF lf;
+    if constexpr (LF::kShared) {
+        // lane L holds pair L (pair p covers elements 2p, 2p + 1)
+        const int e = 2 * lane;
+        lf.ax = e < a.c1 ? 0 : (e < a.c2 ? 1 : 2);
+        lf.f[0] = lane < LPH * VEC / 2 ? a.inv_freq[lane] : 0.f;
+    } else {
+        lf.ax = e0 < a.c1 ? 0 : (e0 < a.c2 ? 1 : 2);
+        const int cstart = lf.ax == 0 ? 0 : (lf.ax == 1 ? a.c1 : a.c2);
+        const int cend = lf.ax == 0 ? a.c1 : (lf.ax == 1 ? a.c2 : a.head_dim);
+        const int chalf = (cend - cstart) / 2;
+#pragma unroll
+        for (int m = 0; m < LF::NA; ++m) {
+            const int pair = HALF ? cstart / 2 + ((e0 - cstart + m) % chalf) : e0 / 2 + m;
+            lf.f[m] = a.inv_freq[pair];
+        }
+    }
+    return lf;
+}
+
+// One lane's share of one head-row of a token at position (pt, ph, pw): RMSNorm
+// of the head (a DPP reduction over its LPH lanes) times the weight, then the
+// 3D rotation of the lane's pairs.  o receives the rotated values in fp32
+// (rounded by the caller).
+template <typename T, int VEC, int LPH, bool HALF>
+__device__ __forceinline__ void qk_token(const QKArgs& a, int32_t pt, int32_t ph, int32_t pw,
+                                         int lane, int e0, const LaneFreq<VEC, LPH, HALF>& lf,
+                                         const float (&w)[VEC], const Vec<T, VEC>& buf,
+                                         float (&o)[VEC]) {
+    using LF = LaneFreq<VEC, LPH, HALF>;
+    constexpr int NA = LF::NA;
+    const float pf = (float)(lf.ax == 0 ? pt : (lf.ax == 1 ? ph : pw));
+    float cs[NA], sn[NA];
+    if constexpr (LF::kShared) {
+        float s1 = 0.f, c1 = 1.f;
+        if (lane < LPH * VEC / 2) sincosf(pf * lf.f[0], &s1, &c1);
+#pragma unroll
+        for (int m = 0; m < NA; ++m) {
+            cs[m] = __shfl(c1, e0 / 2 + m, 64);
+            sn[m] = __shfl(s1, e0 / 2 + m, 64);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < NA; ++m) sincosf(pf * lf.f[m], &sn[m], &cs[m]);
+    }
+
+    float v[VEC];
+    buf.to_float(v);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+    ss = group_sum<LPH>(ss);
+    const float rstd = __builtin_amdgcn_rsqf(ss * a.inv_head_dim + a.eps);
+    float u[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) u[i] = v[i] * rstd * w[i];
+    if constexpr (!HALF) {
+#pragma unroll
+        for (int m = 0; m < VEC / 2; ++m) {
+            const float u0 = u[2 * m], u1 = u[2 * m + 1];
+            o[2 * m] = u0 * cs[m] - u1 * sn[m];
+            o[2 * m + 1] = u0 * sn[m] + u1 * cs[m];
+        }
+    } else {
+        // pairs (j, j + d_c/2): the partner chunk sits chalf / VEC lanes away
+        const int cstart = lf.ax == 0 ? 0 : (lf.ax == 1 ? a.c1 : a.c2);
+        const int cend = lf.ax == 0 ? a.c1 : (lf.ax == 1 ? a.c2 : a.head_dim);
+        const int chalf = (cend - cstart) / 2;
+        const bool first = (e0 - cstart) < chalf;
+        const int partner = first ? lane + chalf / VEC : lane - chalf / VEC;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const float pv = __shfl(u[i], partner, 64);
+            o[i] = first ? u[i] * cs[i] - pv * sn[i] : pv * sn[i] + u[i] * cs[i];
+        }
+    }
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void load_weights(const char* wp, int e0, float (&w)[VEC]) {
+    Vec<T, VEC> t;
+    t.template load<false>(reinterpret_cast<const T*>(wp) + e0);
+    t.to_float(w);
+}
+
 template <typename T, int VEC, int LPH, bool HALF>
 __global__ void __launch_bounds__(64) qk_rmsnorm_rope3d_kernel(QKArgs a) {
     constexpr int GPW = 64 / LPH;             // head-rows per wavefront load
-    constexpr int NA = HALF ? VEC : VEC / 2;  // rotation pairs touched by a lane
-    constexpr bool kShared = !HALF && LPH * VEC / 2 <= 64;
     const int lane = threadIdx.x;
     const int gsub = lane / LPH;        // head-row slot of this lane
     const int e0 = (lane % LPH) * VEC;  // first element of the lane in its head
@@ -114,78 +216,170 @@ __global__ void __launch_bounds__(64) qk_rmsnorm_rope3d_kernel(QKArgs a) {
     buf.template load_buf<kLoadStream>(rin, hd * (uint32_t)(isk ? a.k_hs : a.q_hs) + e0b);
 
     float w[VEC];
-    {
-        Vec<T, VEC> t;
-        t.template load<false>(reinterpret_cast<const T*>(isk ? a.kw : a.qw) + e0);
-        t.to_float(w);
-    }
-
-    // Angles of the lane's rotation pairs at this token.
+    load_weights<T, VEC>(isk ? a.kw : a.qw, e0, w);
+    const LaneFreq<VEC, LPH, HALF> lf = lane_freq<VEC, LPH, HALF>(a, lane, e0);
     int32_t pt, ph, pw;
     token_position(a.grid, row, pt, ph, pw);
-    float cs[NA], sn[NA];
-    if constexpr (kShared) {
-        // lane L holds pair L (pair p covers elements 2p, 2p + 1)
-        const int e = 2 * lane;
-        const int ax = e < a.c1 ? 0 : (e < a.c2 ? 1 : 2);
-        const float pf = (float)(ax == 0 ? pt : (ax == 1 ? ph : pw));
-        float s1 = 0.f, c1 = 1.f;
-        if (lane < LPH * VEC / 2) sincosf(pf * a.inv_freq[lane], &s1, &c1);
-#pragma unroll
-        for (int m = 0; m < NA; ++m) {
-            cs[m] = __shfl(c1, e0 / 2 + m, 64);
-            sn[m] = __shfl(s1, e0 / 2 + m, 64);
-        }
-    } else {
-        const int ax = e0 < a.c1 ? 0 : (e0 < a.c2 ? 1 : 2);
-        const int cstart = ax == 0 ? 0 : (ax == 1 ? a.c1 : a.c2);
-        const int cend = ax == 0 ? a.c1 : (ax == 1 ? a.c2 : a.head_dim);
-        const int chalf = (cend - cstart) / 2;
-        const float pf = (float)(ax == 0 ? pt : (ax == 1 ? ph : pw));
-#pragma unroll
-        for (int m = 0; m < NA; ++m) {
-            const int pair = HALF ? cstart / 2 + ((e0 - cstart + m) % chalf) : e0 / 2 + m;
-            sincosf(pf * a.inv_freq[pair], &sn[m], &cs[m]);
-        }
-    }
-
-    float v[VEC];
-    buf.to_float(v);
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
-    ss = group_sum<LPH>(ss);
-    const float rstd = __builtin_amdgcn_rsqf(ss * a.inv_head_dim + a.eps);
-    float u[VEC];
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) u[i] = v[i] * rstd * w[i];
     float o[VEC];
-    if constexpr (!HALF) {
-#pragma unroll
-        for (int m = 0; m < VEC / 2; ++m) {
-            const float u0 = u[2 * m], u1 = u[2 * m + 1];
-            o[2 * m] = u0 * cs[m] - u1 * sn[m];
-            o[2 * m + 1] = u0 * sn[m] + u1 * cs[m];
-        }
-    } else {
-        // pairs (j, j + d_c/2): the partner chunk sits chalf / VEC lanes away
-        const int ax = e0 < a.c1 ? 0 : (e0 < a.c2 ? 1 : 2);
-        const int cstart = ax == 0 ? 0 : (ax == 1 ? a.c1 : a.c2);
-        const int cend = ax == 0 ? a.c1 : (ax == 1 ? a.c2 : a.head_dim);
-        const int chalf = (cend - cstart) / 2;
-        const bool first = (e0 - cstart) < chalf;
-        const int partner = first ? lane + chalf / VEC : lane - chalf / VEC;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            const float pv = __shfl(u[i], partner, 64);
-            o[i] = first ? u[i] * cs[i] - pv * sn[i] : pv * sn[i] + u[i] * cs[i];
-        }
-    }
+    qk_token<T, VEC, LPH, HALF>(a, pt, ph, pw, lane, e0, lf, w, buf, o);
     Vec<T, VEC> ov;
     ov.from_float(o);
     const rsrc_t rout = isk ? make_rsrc(a.k_out + row * a.ko_rs, a.ko_span)
                             : make_rsrc(a.q_out + row * a.qo_rs, a.qo_span);
     ov.template store_buf<kStoreStream>(rout, hd * (uint32_t)(isk ? a.ko_hs : a.qo_hs) + e0b);
+}
+
+// Router pooling fused into the operator.  The block-sparse router ranks key
+// blocks by the means of the post-RoPE q and k over blocks of `block` tokens;
+// computed here, from the values as stored, they cost no second pass over q
+// and k.  One workgroup of kPoolWaves wavefronts per (tensor, token block,
+// head-row slot): wavefront v takes the block's chunks of kPoolTokens tokens
+// v, v + kPoolWaves, ... (a chunk's loads in flight together), does for each
+// token exactly what qk_rmsnorm_rope3d_kernel does (same code, so the stored
+// outputs are bit-identical) and adds the stored, rounded values into fp32
+// sums; the wavefronts' sums are added in wavefront order through LDS and
+// their means go to pooled[tensor][head][block][head_dim], the router's
+// workspace layout.  Many wavefronts per block are needed: a token's work is a
+// chain of dependent steps (sincos, lane shuffles, the RMS reduction), and one
+// wavefront walking a whole block alone left the chip mostly waiting on them.
+// Measured at the 5 s shape (tokens per chunk x wavefronts): 8 x 1 1.03 ms,
+// 8 x 4 0.99, 4 x 8 0.95, 2 x 8 0.92, 1 x 16 0.93, 2 x 16 0.91 (the plain
+// operator alone: 0.80 ms, plus 0.41 ms for the router's separate pooling).
+constexpr int kPoolTokens = 2;
+constexpr int kPoolWaves = 16;
+
+struct PoolOut {
+    float* pooled;        // [2][heads][n_blocks][head_dim] fp32
+    int64_t rows;
+    int32_t block;
+    int32_t heads;
+    uint32_t n_blocks;
+    uint32_t n_q_blocks;  // n_blocks * nl: workgroups [0, n) are q, [n, 2n) are k
+};
+
+template <typename T, int VEC, int LPH, bool HALF>
+__global__ void __launch_bounds__(64 * kPoolWaves) qk_pool_kernel(QKArgs a, PoolOut p) {
+    constexpr int GPW = 64 / LPH;
+    constexpr int U = kPoolTokens;
+    constexpr int NW = kPoolWaves;
+    __shared__ float part[NW - 1][64][VEC];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int gsub = lane / LPH;
+    const int e0 = (lane % LPH) * VEC;
+    const uint32_t bid = blockIdx.x;
+    const bool isk = bid >= p.n_q_blocks;
+    const uint32_t bb = isk ? bid - p.n_q_blocks : bid;
+    const uint32_t b = fdiv(bb, a.div_nl);
+    const uint32_t slot = bb - b * (uint32_t)a.nl;
+    const uint32_t hd = slot * GPW + gsub;
+    // A resource here spans several token rows, so a head slot past the last
+    // head is not out of range: such lanes read head 0 and store nothing.
+    const bool live = hd < (uint32_t)p.heads;
+    const uint32_t e0b = (uint32_t)e0 * sizeof(T);
+    const char* in = isk ? a.k : a.q;
+    const int64_t in_rs = isk ? a.k_rs : a.q_rs;
+    const uint32_t in_span = isk ? a.k_span : a.q_span;
+    const uint32_t in_off = (live ? hd : 0u) * (uint32_t)(isk ? a.k_hs : a.q_hs) + e0b;
+    char* out = isk ? a.k_out : a.q_out;
+    const int64_t out_rs = isk ? a.ko_rs : a.qo_rs;
+    const uint32_t out_span = isk ? a.ko_span : a.qo_span;
+    const uint32_t out_off = (live ? hd : 0u) * (uint32_t)(isk ? a.ko_hs : a.qo_hs) + e0b;
+
+    float w[VEC];
+    load_weights<T, VEC>(isk ? a.kw : a.qw, e0, w);
+    const LaneFreq<VEC, LPH, HALF> lf = lane_freq<VEC, LPH, HALF>(a, lane, e0);
+    const int64_t r_begin = (int64_t)b * p.block;
+    const int64_t r_end = r_begin + p.block < p.rows ? r_begin + p.block : p.rows;
+    float sum[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) sum[i] = 0.f;
+    // Chunks of U tokens, double-buffered: chunk c + 1 is loaded before chunk c
+    // is computed and stored, so waiting for a chunk's loads never includes the
+    // previous chunk's stores (the vector memory counter counts both, in
+    // order).  The last chunk loads itself again, so every step issues the
+    // same number of loads and the waits stay fixed.
+    const int nchunks = (int)((r_end - r_begin + U - 1) / U);
+    // Every chunk issues the same memory operations -- U loads, one positions
+    // load (a zero-length resource when positions are derived) and U stores
+    // (dropped past the block's last token or for a head past the last) -- so
+    // the waits between chunks stay exact.  The prefetch after a wavefront's
+    // last chunk goes to a zero-length resource: issued, but it moves no bytes.  Explicit positions are read with
+    // their chunk's data: 3 int32 per token, one 12-byte load by lanes
+    // 0 .. U-1, handed to the other lanes by shuffles.
+    const int32_t* posp = a.grid.positions;
+    auto load_chunk = [&](int c, bool real, Vec<T, VEC> (&bf)[U], u32x3& pos) {
+        const int64_t r0 = r_begin + (int64_t)c * U;
+        const int n = (int)(r_end - r0 < U ? r_end - r0 : U);
+        // rows past the block's last read as zeros (outside the resource)
+        const rsrc_t rin = make_rsrc(in + r0 * in_rs,
+                                     real ? (uint32_t)((n - 1) * in_rs) + in_span : 0u);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            bf[u].template load_buf<kLoadStream>(rin, (uint32_t)(u * in_rs) + in_off);
+        const rsrc_t rp = make_rsrc(posp ? posp + 3 * r0 : posp, posp && real ? (uint32_t)n * 12u : 0u);
+        pos = __builtin_bit_cast(
+            u32x3, __builtin_amdgcn_raw_buffer_load_b96(rp, (uint32_t)(lane & (U - 1)) * 12u, 0, 0));
+    };
+    auto process = [&](int c, const Vec<T, VEC> (&bf)[U], const u32x3& pos) {
+        const int64_t r0 = r_begin + (int64_t)c * U;
+        const int n = (int)(r_end - r0 < U ? r_end - r0 : U);
+        const rsrc_t rout = make_rsrc(out + r0 * out_rs, (uint32_t)((n - 1) * out_rs) + out_span);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int32_t pt, ph, pw;
+            if (posp) {
+                pt = __shfl((int)pos[0], u, 64);
+                ph = __shfl((int)pos[1], u, 64);
+                pw = __shfl((int)pos[2], u, 64);
+            } else {
+                token_position(a.grid, r0 + u, pt, ph, pw);
+            }
+            float o[VEC];
+            qk_token<T, VEC, LPH, HALF>(a, pt, ph, pw, lane, e0, lf, w, bf[u], o);
+            Vec<T, VEC> ov;
+            ov.from_float(o);
+            ov.template store_buf<kStoreStream>(
+                rout, u < n && live ? (uint32_t)(u * out_rs) + out_off : kDroppedOffset);
+            if (u < n) {
+                float st[VEC];
+                ov.to_float(st);  // the mean is of the stored values
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) sum[i] += st[i];
+            }
+        }
+    };
+    Vec<T, VEC> buf0[U], buf1[U];
+    u32x3 pos0, pos1;
+    // this wavefront's chunks: wv, wv + NW, ... (a wavefront with none loads
+    // chunk 0 and computes nothing)
+    load_chunk(wv < nchunks ? wv : 0, wv < nchunks, buf0, pos0);
+    for (int c = wv; c < nchunks; c += 2 * NW) {
+        load_chunk(c + NW < nchunks ? c + NW : c, c + NW < nchunks, buf1, pos1);
+        process(c, buf0, pos0);
+        if (c + NW >= nchunks) break;
+        load_chunk(c + 2 * NW < nchunks ? c + 2 * NW : c + NW, c + 2 * NW < nchunks, buf0, pos0);
+        process(c + NW, buf1, pos1);
+    }
+    // add the wavefronts' sums in wavefront order
+    if (wv > 0) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) part[wv - 1][lane][i] = sum[i];
+    }
+    __syncthreads();
+    if (wv > 0) return;
+#pragma unroll
+    for (int v = 0; v < NW - 1; ++v)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) sum[i] += part[v][lane][i];
+    if (!live) return;
+    const float nt = (float)(r_end - r_begin);
+    float* dst = p.pooled +
+                 (((size_t)(isk ? 1 : 0) * p.heads + hd) * p.n_blocks + b) * (size_t)a.head_dim + e0;
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4)
+        *reinterpret_cast<float4*>(dst + i) =
+            make_float4(sum[i] / nt, sum[i + 1] / nt, sum[i + 2] / nt, sum[i + 3] / nt);
 }
 
 __global__ void __launch_bounds__(256) positions_kernel(int32_t* __restrict__ pos, int64_t rows,
@@ -276,20 +470,29 @@ extern "C" h3f_status_t h3f_rope3d_positions(int32_t* pos, int64_t rows, const h
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }
 
-extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
-    void* q_out, int64_t q_out_row_stride, int64_t q_out_head_stride, void* k_out,
-    int64_t k_out_row_stride, int64_t k_out_head_stride, const void* q, int64_t q_row_stride,
-    int64_t q_head_stride, const void* k, int64_t k_row_stride, int64_t k_head_stride,
-    const void* q_weight, const void* k_weight, h3f_dtype_t dtype, int64_t rows, int32_t heads,
-    int32_t head_dim, float eps, const h3f_rope3d_t* rope, void* stream) {
-    if (rows == 0) return H3F_OK;
+namespace {
+
+// Regions of the tensors of one call, for the fused form's extra checks.
+struct QKRegions {
+    Region qo, ko, q, k, qw, kw;
+};
+
+// Validation of a QK RMSNorm + RoPE call and its kernel arguments (shared by
+// the plain and the pooled entry points); rows >= 1.
+h3f_status_t qk_prepare(QKArgs& a, int& lph, QKRegions& reg, void* q_out, int64_t q_out_row_stride,
+                        int64_t q_out_head_stride, void* k_out, int64_t k_out_row_stride,
+                        int64_t k_out_head_stride, const void* q, int64_t q_row_stride,
+                        int64_t q_head_stride, const void* k, int64_t k_row_stride,
+                        int64_t k_head_stride, const void* q_weight, const void* k_weight,
+                        h3f_dtype_t dtype, int64_t rows, int32_t heads, int32_t head_dim,
+                        float eps, const h3f_rope3d_t* rope) {
     if (!q_out || !k_out || !q || !k || !q_weight || !k_weight || !rope)
         return H3F_ERR_NULL_POINTER;
     if (!dtype_ok(dtype)) return H3F_ERR_BAD_DTYPE;
     if (rows < 0 || heads < 1 || head_dim < 1) return H3F_ERR_BAD_SHAPE;
     const int V = vec_width(dtype == H3F_F32);
     if (head_dim % V) return H3F_ERR_BAD_SHAPE;
-    const int lph = head_dim / V;
+    lph = head_dim / V;
     if (lph < 2 || lph > 64 || (lph & (lph - 1))) return H3F_ERR_UNSUPPORTED;
     if (rope->d_t < V || rope->d_h < V || rope->d_w < V || rope->d_t % V || rope->d_h % V ||
         rope->d_w % V || rope->d_t + rope->d_h + rope->d_w != head_dim)
@@ -363,7 +566,6 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
     if (same_region(rko, rk) && heads > 1 && k_out_head_stride != k_head_stride)
         return H3F_ERR_ALIASING;
 
-    QKArgs a{};
     a.q_out = static_cast<char*>(q_out);
     a.qo_rs = q_out_row_stride * e;
     a.qo_hs = (heads > 1 ? q_out_head_stride : head_dim) * e;
@@ -398,6 +600,35 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
     for (int c = 0; c < 3; ++c)
         for (int32_t j = 0; j < dims[c] / 2; ++j)
             a.inv_freq[p++] = (float)pow(rope->theta, -2.0 * (double)j / (double)dims[c]);
+    reg = QKRegions{rqo, rko, rq, rk, rw1, rw2};
+    return H3F_OK;
+}
+
+template <bool HALF>
+hipError_t launch_pool(const QKArgs& a, const PoolOut& p, hipStream_t st) {
+    hipLaunchKernelGGL((qk_pool_kernel<__bf16, 8, 16, HALF>), dim3(2 * p.n_q_blocks),
+                       dim3(64 * kPoolWaves), 0, st, a, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
+    void* q_out, int64_t q_out_row_stride, int64_t q_out_head_stride, void* k_out,
+    int64_t k_out_row_stride, int64_t k_out_head_stride, const void* q, int64_t q_row_stride,
+    int64_t q_head_stride, const void* k, int64_t k_row_stride, int64_t k_head_stride,
+    const void* q_weight, const void* k_weight, h3f_dtype_t dtype, int64_t rows, int32_t heads,
+    int32_t head_dim, float eps, const h3f_rope3d_t* rope, void* stream) {
+    if (rows == 0) return H3F_OK;
+    QKArgs a{};
+    int lph = 0;
+    QKRegions reg;
+    const h3f_status_t s = qk_prepare(a, lph, reg, q_out, q_out_row_stride, q_out_head_stride,
+                                      k_out, k_out_row_stride, k_out_head_stride, q,
+                                      q_row_stride, q_head_stride, k, k_row_stride,
+                                      k_head_stride, q_weight, k_weight, dtype, rows, heads,
+                                      head_dim, eps, rope);
+    if (s != H3F_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool half = rope->pairing == H3F_ROPE_HALF_SPLIT;
     hipError_t err;
@@ -407,5 +638,55 @@ extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d(
     else
         err = half ? dispatch_lph<float, 4, true>(a, lph, rows, st)
                    : dispatch_lph<float, 4, false>(a, lph, rows, st);
+    return err == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
+}
+
+extern "C" h3f_status_t h3f_qk_rmsnorm_rope3d_pool(
+    void* q_out, int64_t q_out_row_stride, int64_t q_out_head_stride, void* k_out,
+    int64_t k_out_row_stride, int64_t k_out_head_stride, const void* q, int64_t q_row_stride,
+    int64_t q_head_stride, const void* k, int64_t k_row_stride, int64_t k_head_stride,
+    const void* q_weight, const void* k_weight, h3f_dtype_t dtype, int64_t rows, int32_t heads,
+    int32_t head_dim, float eps, const h3f_rope3d_t* rope, int32_t block, void* workspace,
+    size_t workspace_bytes, void* stream) {
+    if (!q_out || !k_out || !q || !k || !q_weight || !k_weight || !rope)
+        return H3F_ERR_NULL_POINTER;
+    // the router's preconditions (bf16, head_dim 128, rows >= 4096, block and
+    // head counts) and its workspace size
+    int32_t nb = 0;
+    size_t need = 0;
+    h3f_status_t s = h3f_subblock_plan(rows, heads, head_dim, block, 0.0,
+                                       H3F_SUBBLOCK_FIRST_STEP, &nb, nullptr, &need);
+    if (s != H3F_OK) return s;
+    if (!dtype_ok(dtype)) return H3F_ERR_BAD_DTYPE;
+    if (dtype != H3F_BF16) return H3F_ERR_UNSUPPORTED;
+    QKArgs a{};
+    int lph = 0;
+    QKRegions reg;
+    s = qk_prepare(a, lph, reg, q_out, q_out_row_stride, q_out_head_stride, k_out,
+                   k_out_row_stride, k_out_head_stride, q, q_row_stride, q_head_stride, k,
+                   k_row_stride, k_head_stride, q_weight, k_weight, dtype, rows, heads, head_dim,
+                   eps, rope);
+    if (s != H3F_OK) return s;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return H3F_ERR_WORKSPACE;
+    const Region rws = region2d(workspace, 1, 0, (int64_t)need, 1);
+    const Region* others[] = {&reg.qo, &reg.ko, &reg.q, &reg.k, &reg.qw, &reg.kw};
+    for (const Region* o : others)
+        if (!disjoint(rws, *o)) return H3F_ERR_ALIASING;
+    // kPoolTokens rows of a tensor are addressed through one 32-bit resource
+    const int64_t rs_max = std::max(std::max(a.q_rs, a.k_rs), std::max(a.qo_rs, a.ko_rs));
+    const int64_t span_max = std::max(std::max(reg.q.span, reg.k.span),
+                                      std::max(reg.qo.span, reg.ko.span));
+    if (rs_max > (0xFFFFFFF0ll - span_max) / kPoolTokens) return H3F_ERR_UNSUPPORTED;
+
+    PoolOut p;
+    p.pooled = static_cast<float*>(workspace);
+    p.rows = rows;
+    p.block = block;
+    p.heads = heads;
+    p.n_blocks = (uint32_t)nb;
+    p.n_q_blocks = (uint32_t)nb * (uint32_t)a.nl;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t err = rope->pairing == H3F_ROPE_HALF_SPLIT ? launch_pool<true>(a, p, st)
+                                                                 : launch_pool<false>(a, p, st);
     return err == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }

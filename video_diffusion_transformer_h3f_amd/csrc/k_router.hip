@@ -629,6 +629,50 @@ h3f_status_t check_plan(int64_t rows, int32_t heads, int32_t head_dim, int32_t b
     return H3F_OK;
 }
 
+// Block scores from the pooled means, then the kept lists (routed steps).
+void launch_score_select(const float* pooled, float* scores, int32_t* kv_blocks, int32_t heads,
+                         int64_t nb, int64_t keep, hipStream_t s) {
+    ScoreArgs sa;
+    sa.pooled = pooled;
+    sa.scores = scores;
+    sa.heads = heads;
+    sa.nb = (uint32_t)nb;
+    sa.tiles = (uint32_t)((nb + kTile - 1) / kTile);
+    const dim3 scg((unsigned)(heads * sa.tiles * ((sa.tiles + kScoreRun - 1) / kScoreRun)));
+    if (nb % 4 == 0)
+        hipLaunchKernelGGL(subblock_score_kernel<16>, scg, dim3(256), 0, s, sa);
+    else if (nb % 2 == 0)
+        hipLaunchKernelGGL(subblock_score_kernel<8>, scg, dim3(256), 0, s, sa);
+    else
+        hipLaunchKernelGGL(subblock_score_kernel<4>, scg, dim3(256), 0, s, sa);
+
+    SelectArgs se;
+    se.scores = scores;
+    se.kv = kv_blocks;
+    se.rows = (uint32_t)(heads * nb);
+    se.nb = (uint32_t)nb;
+    se.keep = (uint32_t)keep;
+    const dim3 sg((se.rows + kSelWaves - 1) / kSelWaves), sb(64 * kSelWaves);
+    if (nb <= 64 * 4)
+        hipLaunchKernelGGL(subblock_select_kernel<4>, sg, sb, 0, s, se);
+    else if (nb <= 64 * 16)
+        hipLaunchKernelGGL(subblock_select_kernel<16>, sg, sb, 0, s, se);
+    else if (nb <= 64 * 32)
+        hipLaunchKernelGGL(subblock_select_kernel<32>, sg, sb, 0, s, se);
+    else
+        hipLaunchKernelGGL(subblock_select_kernel<128>, sg, sb, 0, s, se);
+}
+
+// Every block kept (dense steps): kv[h, i, :] = 0 .. nb - 1.
+h3f_status_t launch_dense(int32_t* kv_blocks, int32_t heads, int64_t nb, int64_t keep,
+                          hipStream_t s) {
+    const uint64_t total = (uint64_t)heads * nb * keep;
+    const unsigned blocks = (unsigned)std::min<uint64_t>((total + 255) / 256, 65536);
+    hipLaunchKernelGGL(subblock_dense_kernel, dim3(blocks), dim3(256), 0, s, kv_blocks,
+                       (uint32_t)nb, total);
+    return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
+}
+
 }  // namespace
 }  // namespace h3f
 
@@ -706,13 +750,7 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
         return H3F_ERR_ALIASING;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const uint64_t total = (uint64_t)heads * nb * keep;
-    if (!routed) {
-        const unsigned blocks = (unsigned)std::min<uint64_t>((total + 255) / 256, 65536);
-        hipLaunchKernelGGL(subblock_dense_kernel, dim3(blocks), dim3(256), 0, s, kv_blocks,
-                           (uint32_t)nb, total);
-        return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
-    }
+    if (!routed) return launch_dense(kv_blocks, heads, nb, keep, s);
 
     PoolArgs pa;
     pa.base[0] = static_cast<const char*>(q);
@@ -754,34 +792,33 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
                            dim3(2 * pa.n_blocks * pa.n_groups), dim3(64 * kPoolWaves), 0, s, pa);
     }
 
-    ScoreArgs sa;
-    sa.pooled = pa.pooled;
-    sa.scores = scores;
-    sa.heads = heads;
-    sa.nb = (uint32_t)nb;
-    sa.tiles = (uint32_t)((nb + kTile - 1) / kTile);
-    const dim3 scg((unsigned)(heads * sa.tiles * ((sa.tiles + kScoreRun - 1) / kScoreRun)));
-    if (nb % 4 == 0)
-        hipLaunchKernelGGL(subblock_score_kernel<16>, scg, dim3(256), 0, s, sa);
-    else if (nb % 2 == 0)
-        hipLaunchKernelGGL(subblock_score_kernel<8>, scg, dim3(256), 0, s, sa);
-    else
-        hipLaunchKernelGGL(subblock_score_kernel<4>, scg, dim3(256), 0, s, sa);
+    launch_score_select(pa.pooled, scores, kv_blocks, heads, nb, keep, s);
+    return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
+}
 
-    SelectArgs se;
-    se.scores = scores;
-    se.kv = kv_blocks;
-    se.rows = (uint32_t)(heads * nb);
-    se.nb = (uint32_t)nb;
-    se.keep = (uint32_t)keep;
-    const dim3 sg((se.rows + kSelWaves - 1) / kSelWaves), sb(64 * kSelWaves);
-    if (nb <= 64 * 4)
-        hipLaunchKernelGGL(subblock_select_kernel<4>, sg, sb, 0, s, se);
-    else if (nb <= 64 * 16)
-        hipLaunchKernelGGL(subblock_select_kernel<16>, sg, sb, 0, s, se);
-    else if (nb <= 64 * 32)
-        hipLaunchKernelGGL(subblock_select_kernel<32>, sg, sb, 0, s, se);
-    else
-        hipLaunchKernelGGL(subblock_select_kernel<128>, sg, sb, 0, s, se);
+extern "C" h3f_status_t h3f_subblock_route_pooled(int32_t* kv_blocks, float* scores, int64_t rows,
+                                                  int32_t heads, int32_t head_dim, int32_t block,
+                                                  double sparsity, int32_t step,
+                                                  const void* workspace, size_t workspace_bytes,
+                                                  void* stream) {
+    if (!kv_blocks || !scores) return H3F_ERR_NULL_POINTER;
+    const h3f_status_t st = check_plan(rows, heads, head_dim, block, sparsity, step);
+    if (st != H3F_OK) return st;
+    if (!aligned16(scores)) return H3F_ERR_MISALIGNED;
+    if (reinterpret_cast<uintptr_t>(kv_blocks) & 3u) return H3F_ERR_MISALIGNED;
+    const int64_t nb = ceil_div(rows, block);
+    const int64_t keep = keep_for(nb, sparsity, step);
+    const size_t need = workspace_for(nb, heads);
+    const bool routed = step >= H3F_SUBBLOCK_FIRST_STEP;
+    if (routed && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+        return H3F_ERR_WORKSPACE;
+    const Region rkv = region2d(kv_blocks, 1, 0, (int64_t)heads * nb * keep * 4, 1);
+    const Region rsc = region2d(scores, 1, 0, (int64_t)heads * nb * nb * 4, 1);
+    const Region rws = region2d(workspace, 1, 0, routed ? (int64_t)need : 0, 1);
+    if (!disjoint(rkv, rws) || (routed && (!disjoint(rkv, rsc) || !disjoint(rsc, rws))))
+        return H3F_ERR_ALIASING;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!routed) return launch_dense(kv_blocks, heads, nb, keep, s);
+    launch_score_select(static_cast<const float*>(workspace), scores, kv_blocks, heads, nb, keep, s);
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }
