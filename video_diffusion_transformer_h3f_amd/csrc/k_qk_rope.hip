@@ -294,19 +294,18 @@ __global__ void __launch_bounds__(64 * kPoolWaves) qk_pool_kernel(QKArgs a, Pool
     float sum[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) sum[i] = 0.f;
-    // Chunks of U tokens, double-buffered: chunk c + 1 is loaded before chunk c
-    // is computed and stored, so waiting for a chunk's loads never includes the
-    // previous chunk's stores (the vector memory counter counts both, in
-    // order).  The last chunk loads itself again, so every step issues the
-    // same number of loads and the waits stay fixed.
+    // Chunks of U tokens, double-buffered: a wavefront loads its next chunk
+    // before it computes and stores the current one, so waiting for a chunk's
+    // loads never includes the previous chunk's stores (the vector memory
+    // counter counts both, in order).  Every chunk issues the same memory
+    // operations -- U loads, one positions load and U stores -- so those waits
+    // stay exact: stores past the block's last token or for a head past the
+    // last are dropped (offset outside the resource), derived positions and the
+    // prefetch after a wavefront's last chunk use zero-length resources (issued,
+    // moving no bytes).  Explicit positions are read with their chunk's data: 3
+    // int32 per token, one 12-byte load by lanes 0 .. U-1, handed to the other
+    // lanes by shuffles.
     const int nchunks = (int)((r_end - r_begin + U - 1) / U);
-    // Every chunk issues the same memory operations -- U loads, one positions
-    // load (a zero-length resource when positions are derived) and U stores
-    // (dropped past the block's last token or for a head past the last) -- so
-    // the waits between chunks stay exact.  The prefetch after a wavefront's
-    // last chunk goes to a zero-length resource: issued, but it moves no bytes.  Explicit positions are read with
-    // their chunk's data: 3 int32 per token, one 12-byte load by lanes
-    // 0 .. U-1, handed to the other lanes by shuffles.
     const int32_t* posp = a.grid.positions;
     auto load_chunk = [&](int c, bool real, Vec<T, VEC> (&bf)[U], u32x3& pos) {
         const int64_t r0 = r_begin + (int64_t)c * U;
