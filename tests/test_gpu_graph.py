@@ -2,9 +2,10 @@
 
 One DiT block's calls (AdaLN, QK RMSNorm + 3D RoPE, gated residual, AdaLN,
 SwiGLU, gated residual), the residual-difference reduction and the block-sparse
-router are captured once with torch.cuda.graph (the binding launches on the
-current stream, which is the capture stream inside the context) and replayed
-several times, with eager work and synchronisations between the replays.  Every
+router (separate, and with its pooling fused into QK) are captured once with
+torch.cuda.graph (the binding launches on the current stream, which is the
+capture stream inside the context) and replayed several times, with eager work
+and synchronisations between the replays.  Every
 replay must reproduce the eager calls bit for bit, and a replay after the
 inputs change must follow the new contents (the graph holds pointers, not
 data).  The library issues kernel launches only (no memset, copy or allocation
@@ -54,11 +55,16 @@ def _buffers():
         "l1": torch.empty(3, dtype=torch.float64, device=DEV),
         "kv": torch.empty(H, nb, keep, dtype=torch.int32, device=DEV),
         "scores": torch.empty(H, nb, nb, dtype=torch.float32, device=DEV),
+        "q_out2": torch.empty(ROWS, H, Dh, dtype=torch.bfloat16, device=DEV),
+        "k_out2": torch.empty(ROWS, H, Dh, dtype=torch.bfloat16, device=DEV),
+        "kv2": torch.empty(H, nb, keep, dtype=torch.int32, device=DEV),
+        "scores2": torch.empty(H, nb, nb, dtype=torch.float32, device=DEV),
         "x": t["x"],
     }
     t["l1_ws"] = torch.empty(max(h3.h3f_residual_l1_workspace_bytes(ROWS, D, torch.bfloat16), 16),
                              dtype=torch.uint8, device=DEV)
     t["route_ws"] = torch.empty(max(ws, 16), dtype=torch.uint8, device=DEV)
+    t["pool_ws"] = torch.empty(max(ws, 16), dtype=torch.uint8, device=DEV)
     return t, outs
 
 
@@ -74,6 +80,11 @@ def _block(t, o, rope):
     h3.h3f_residual_l1(o["l1"], t["x"], t["x_prev"], workspace=t["l1_ws"])
     h3.h3f_subblock_route(o["kv"], o["scores"], o["q_out"], o["k_out"], 128, 0.8, 12,
                           workspace=t["route_ws"])
+    # the same route with the pooling fused into the QK operator
+    h3.h3f_qk_rmsnorm_rope3d_pool(o["q_out2"], o["k_out2"], t["q"], t["k"], t["q_weight"],
+                                  t["k_weight"], rope, 128, t["pool_ws"])
+    h3.h3f_subblock_route_pooled(o["kv2"], o["scores2"], ROWS, S5["heads"], 128, 0.8, 12,
+                                 t["pool_ws"])
 
 
 def _snapshot(o):
