@@ -58,3 +58,12 @@ def test_router_bytes():
     nb, keep = 978, 196
     b = bench.router_bytes(N5, C5, nb, keep)
     assert b == 2 * N5 * 40 * 128 * 2 + 40 * nb * nb * 4 + 40 * nb * keep * 4
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
