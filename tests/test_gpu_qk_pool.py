@@ -88,11 +88,14 @@ CASES = [
     (4096, 8, 64, True, h3.H3F_ROPE_HALF_SPLIT, False),
     (5000, 2, 1000, False, h3.H3F_ROPE_INTERLEAVED, True),
     (4096 + 3, 5, 4099, False, h3.H3F_ROPE_INTERLEAVED, False),
+    (4096, 1, 1, False, h3.H3F_ROPE_INTERLEAVED, False),   # one token per block: chunks half empty
+    (4096 + 5, 2, 3, True, h3.H3F_ROPE_HALF_SPLIT, True),  # ragged 3-token blocks, every option
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=["ragged-3heads", "packed-halfsplit",
-                                             "long-blocks-positions", "one-block"])
+                                             "long-blocks-positions", "one-block",
+                                             "block1-one-head", "block3-packed-half-positions"])
 def test_qk_pool_outputs_and_means(case):
     rows, heads, block, packed, pairing, explicit = case
     print(f"qk pool rows={rows} heads={heads} block={block} packed={packed} pairing={pairing} "
