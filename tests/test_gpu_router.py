@@ -149,7 +149,8 @@ def check_selection_valid(kv, ref_scores, tol):
     (4096, 2, 3, False),          # 1366 blocks (the select kernel's 32-key-per-lane form)
     (4096 + 3, 1, 2, False),      # 2050 blocks (its 128-key-per-lane form)
     (4096 + 50, 9, 128, False),   # 9 dense heads: the strided pool form, not the flat one
-], ids=["ragged", "packed", "long-blocks", "one-block", "nb1366", "nb2050", "heads9"])
+    (4470, 2, 128, False),        # 35 blocks: 3 columns past the last 4-column group
+], ids=["ragged", "packed", "long-blocks", "one-block", "nb1366", "nb2050", "heads9", "nb35"])
 @pytest.mark.parametrize("sparsity", [0.8, 0.75])
 def test_router_matches_oracle(rows, heads, block, packed, sparsity):
     print(f"router rows={rows} heads={heads} block={block} packed={packed} s={sparsity}", flush=True)

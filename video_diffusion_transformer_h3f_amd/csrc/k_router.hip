@@ -305,10 +305,19 @@ __device__ __forceinline__ void mfma_tile32_t(f32x4 (&acc)[2][2], const float (&
 // acc[m][n][e] = scores[i0 + 16 m + ri][j0 + 16 n + 4 g + e].  Stores go
 // through a buffer resource over the head's score matrix; an element outside
 // the matrix gets an offset past the resource's end and is dropped, so there
-// is no branch.  SB = bytes per store: 16 when rows start 16-byte aligned
-// (nb % 4 == 0), 8 when nb is even, else 4.  SB is a template parameter so
-// every tile issues a fixed number of stores, and the wait for the next
-// tile's operand loads never has to include this tile's stores.
+// is no branch.  A lane's 4 columns go out as one 16-byte store when all 4 lie
+// inside the row (a multi-dword buffer store needs only dword alignment, so
+// rows that start 4- or 8-byte aligned take it too).  When nb is not a
+// multiple of 4, the one group per row that straddles the row's end is
+// written by extra stores that every group issues and only that one keeps:
+// SB = 8 (nb = 2 mod 4, 2 columns left) adds an 8-byte store, SB = 4 (nb odd,
+// 1 or 3 left) an 8-byte and a 4-byte one.  Every tile thus issues a fixed
+// number of stores in straight-line code, and the wait for the next tile's
+// operand loads never includes them.  Measured at the 5 s shape (978 blocks):
+// two 8-byte stores for every group (each instruction writing every other 8
+// bytes of the rows it touches) 115 us, this form 108 us.  Choosing the store
+// width per tile with a branch was no better than 113 us: where the two store
+// counts meet, the compiler waits for every store before the barrier.
 constexpr uint32_t kDropped = 0xFFFFFFF0u;
 
 template <int SB>
@@ -322,21 +331,21 @@ __device__ __forceinline__ void store_tile32_t(rsrc_t r, uint32_t nb, uint32_t i
             const uint32_t j = j0 + 16 * n + 4 * g;
             const uint32_t off = (i * nb + j) * 4u;
             const f32x4 v = acc[m][n];
-            if constexpr (SB == 16) {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r,
-                                                       i < nb && j < nb ? off : kDropped, 0, 0);
-            } else if constexpr (SB == 8) {
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    const u32x2 w = {__float_as_uint(v[2 * p]), __float_as_uint(v[2 * p + 1])};
-                    __builtin_amdgcn_raw_buffer_store_b64(
-                        w, r, i < nb && j + 2 * p < nb ? off + 8u * p : kDropped, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r,
+                                                   i < nb && j + 3 < nb ? off : kDropped, 0, 0);
+            if constexpr (SB != 16) {
+                const bool straddle = i < nb && j < nb && j + 3 >= nb;
+                const uint32_t left = nb - j;  // columns left in the row (straddle: 1 .. 3)
+                const u32x2 w = {__float_as_uint(v[0]), __float_as_uint(v[1])};
+                __builtin_amdgcn_raw_buffer_store_b64(w, r, straddle && left >= 2 ? off : kDropped,
+                                                      0, 0);
+                if constexpr (SB == 4) {
+                    // the last column of an odd remainder: j (1 left) or j + 2 (3 left)
+                    const float last = left == 3 ? v[2] : v[0];
                     __builtin_amdgcn_raw_buffer_store_b32(
-                        __float_as_uint(v[e]), r, i < nb && j + e < nb ? off + 4u * e : kDropped, 0, 0);
+                        __float_as_uint(last), r,
+                        straddle && (left & 1) ? off + 4u * (left - 1) : kDropped, 0, 0);
+                }
             }
         }
     }
@@ -349,7 +358,7 @@ constexpr int kTileFrags = (kTile / 16) * 8;  // 1 KiB fragments per 64-row key 
 // flight.
 template <int SB>
 __device__ __forceinline__ void wait_own_gather() {
-    constexpr int n = SB == 16 ? 4 : (SB == 8 ? 8 : 16);
+    constexpr int n = SB == 16 ? 4 : (SB == 8 ? 8 : 12);
     __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
