@@ -192,6 +192,34 @@ def test_router_planted_scores_exact(block):
         assert np.array_equal(kv, kv_ref), f"sparsity {sparsity}"
 
 
+def test_router_planted_outliers_exact():
+    # As above, with a few key blocks of +-4096 among values in [-2, 2]: the
+    # select kernel's first probe (the row's mean + z * std, which assumes a
+    # roughly normal row) lands far from the threshold, and the search must still
+    # end on the oracle's kept blocks.  1023 blocks of 8 tokens (16 keys per lane).
+    block, heads = 8, 2
+    rows = 1023 * block
+    nb = 1023
+    rng = np.random.default_rng(23)
+    alpha = rng.integers(-16, 17, size=nb).astype(np.float32) / 8.0
+    alpha[rng.choice(nb, 5, replace=False)] = 4096.0
+    alpha[rng.choice(nb, 3, replace=False)] = -4096.0
+    q = np.zeros((rows, heads, 128), np.float32)
+    k = np.zeros((rows, heads, 128), np.float32)
+    q[:, :, 0] = 1.0
+    sign = np.array([(-1.0) ** h for h in range(heads)], np.float32)
+    k[:, :, 0] = alpha[np.arange(rows) // block][:, None] * sign[None, :]
+    qb = torch.from_numpy(q).to(torch.bfloat16).to(DEV)
+    kb = torch.from_numpy(k).to(torch.bfloat16).to(DEV)
+    qh = qb.cpu().view(torch.int16).numpy().view(np.uint16)
+    kh = kb.cpu().view(torch.int16).numpy().view(np.uint16)
+    for sparsity in (0.8, 0.995, 0.3):
+        kv, sc = run_route(qb, kb, block, sparsity, step=12)
+        kv_ref, sc_ref = oracle.subblock_route(qh, kh, block, sparsity, 12)
+        assert np.array_equal(sc.astype(np.float64), sc_ref)
+        assert np.array_equal(kv, kv_ref), f"sparsity {sparsity}"
+
+
 def test_router_all_scores_equal_keeps_lowest_blocks():
     # zero queries: every score is +0 or -0 (0 times a negative mean), which rank
     # equal, so each query block keeps the lowest-numbered key blocks
