@@ -313,7 +313,9 @@ __device__ __forceinline__ void mfma_tile32_t(f32x4 (&acc)[2][2], const float (&
 // SB = 8 (nb = 2 mod 4, 2 columns left) adds an 8-byte store, SB = 4 (nb odd,
 // 1 or 3 left) an 8-byte and a 4-byte one.  Every tile thus issues a fixed
 // number of stores in straight-line code, and the wait for the next tile's
-// operand loads never includes them.  Measured at the 5 s shape (978 blocks):
+// operand loads never includes them.  The stores keep the default write-back
+// policy: L2 merges the 64-byte row pieces into whole lines (the streaming
+// policies ran 145 and 171 us instead of 111).  Measured at the 5 s shape (978 blocks):
 // two 8-byte stores for every group (each instruction writing every other 8
 // bytes of the rows it touches) 115 us, this form 108 us.  Choosing the store
 // width per tile with a branch was no better than 113 us: where the two store
