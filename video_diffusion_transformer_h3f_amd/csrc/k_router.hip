@@ -315,11 +315,12 @@ __device__ __forceinline__ void mfma_tile32_t(f32x4 (&acc)[2][2], const float (&
 // number of stores in straight-line code, and the wait for the next tile's
 // operand loads never includes them.  The stores keep the default write-back
 // policy: L2 merges the 64-byte row pieces into whole lines (the streaming
-// policies ran 145 and 171 us instead of 111).  Measured at the 5 s shape (978 blocks):
-// two 8-byte stores for every group (each instruction writing every other 8
-// bytes of the rows it touches) 115 us, this form 108 us.  Choosing the store
-// width per tile with a branch was no better than 113 us: where the two store
-// counts meet, the compiler waits for every store before the barrier.
+// policies ran 145 and 171 us instead of 111).  Measured at the 5 s shape
+// (978 blocks): two 8-byte stores for every group (each instruction writing
+// every other 8 bytes of the rows it touches) 115 us, this form 108 us.
+// Choosing the store width per tile with a branch was no better than 113 us:
+// where the two store counts meet, the compiler waits for every store before
+// the barrier.
 constexpr uint32_t kDropped = 0xFFFFFFF0u;
 
 template <int SB>
