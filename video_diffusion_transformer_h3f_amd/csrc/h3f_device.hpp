@@ -207,6 +207,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup order across the XCDs.  Workgroups of a launch are dealt to the 8
+// XCDs round robin (workgroup w runs on XCD w mod 8), each with its own L2.
+// xcd_linear(w, n) renumbers them so that each XCD takes one contiguous run of
+// the n work items instead of every eighth one.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_linear(uint32_t w, uint32_t n) {
+    const uint32_t per = n / kXcds, extra = n % kXcds;
+    const uint32_t x = w % kXcds, slot = w / kXcds;
+    return x < extra ? x * (per + 1) + slot : extra * (per + 1) + (x - extra) * per + slot;
+}
+
+// ---------------------------------------------------------------------------
 // Unsigned 32-bit division by a run-time invariant divisor d >= 1 for
 // dividends n < 2^31: q = (mulhi(n, m) + n) >> s with s = ceil(log2 d) and
 // m = floor(2^32 (2^s - d) / d) + 1 (Granlund & Montgomery, PLDI 1994, sec. 4).

@@ -102,10 +102,14 @@ __device__ __forceinline__ float silu_f(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Tiles are numbered XCD by XCD (each XCD streams one contiguous run of rows):
+// measured at the 5 s shape over 5 interleaved rounds, 1.560-1.564 ms against
+// 1.574-1.581 in the plain order.  The gated residual, the copy and the QK
+// operator keep the plain order, which is faster for them.
 template <typename T, int VEC>
 __global__ void __launch_bounds__(kBlock)
 swiglu_kernel(Stream os, Stream as, Stream bs, FastDiv div_cols, uint32_t n_chunks) {
-    const uint32_t tile0 = blockIdx.x * (uint32_t)kTile;
+    const uint32_t tile0 = xcd_linear(blockIdx.x, gridDim.x) * (uint32_t)kTile;
     const uint32_t row0 = fdiv(tile0, div_cols);
     const rsrc_t ro = tile_rsrc(os, row0);
     const rsrc_t ra = tile_rsrc(as, row0);

@@ -254,16 +254,8 @@ __device__ __forceinline__ void load_row32(float (&dst)[32], rsrc_t r, uint32_t 
     }
 }
 
-// Workgroups are dealt to the 8 XCDs round robin (workgroup w runs on XCD
-// w mod 8).  Tile t = xcd_base + w / 8 gives each XCD one contiguous run of
-// tiles, so the few heads in flight on an XCD share its L2.
-constexpr uint32_t kXcds = 8;
-
-__device__ __forceinline__ uint32_t xcd_linear(uint32_t w, uint32_t n) {
-    const uint32_t per = n / kXcds, extra = n % kXcds;
-    const uint32_t x = w % kXcds, slot = w / kXcds;
-    return x < extra ? x * (per + 1) + slot : extra * (per + 1) + (x - extra) * per + slot;
-}
+// Score tiles are numbered XCD by XCD (xcd_linear), so the few heads in
+// flight on an XCD share its L2.
 
 // Strip form: a workgroup keeps one 64-row tile of Qm in registers and walks
 // a run of kScoreRun 64-column tiles of Km.  Each Km tile (64 rows x 128
