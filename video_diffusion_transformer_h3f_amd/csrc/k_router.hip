@@ -258,41 +258,28 @@ __device__ __forceinline__ void load_row32(float (&dst)[32], rsrc_t r, uint32_t 
 // flight on an XCD share its L2.
 
 // Strip form: a workgroup keeps one 64-row tile of Qm in registers and walks
-// a run of kScoreRun 64-column tiles of Km.  Each Km tile (64 rows x 128
-// floats) is gathered into LDS once per workgroup with 16-byte buffer-to-LDS
-// loads, already in the order the matrix instructions take it: 1 KiB
-// fragments (rows 16 R .. 16 R + 15, columns 16 v .. 16 v + 15) in which lane
-// ri + 16 g holds row 16 R + ri, columns 16 v + 4 g .. + 3.  Every wavefront
-// then reads its operands with linear, conflict-free 16-byte LDS reads, and
-// the two wavefronts that share key columns no longer load them twice.  Two
-// LDS buffers alternate, the next tile's gather in flight during the current
-// tile's matrix instructions (one barrier per tile).  The MFMA is fed Km as
-// its first operand and Qm as its second, so it produces the transposed
-// tile: lane (ri, g) holds scores[i0 + ri][j0 + 4 g .. 4 g + 3], one 16-byte
-// store per 16 x 16 tile.  Rows and column tiles past the last block read
-// zeros and store nothing.  Measured at the 5 s shape: 125 us with the
-// operands pipelined through registers instead, 115 us this way; runs of 4
-// and 16 tiles were slower than 8.
+// a run of kScoreRun 64-column tiles of Km, each in two halves of the
+// contraction (head_dim columns 0..63, then 64..127).  Each half tile (64
+// rows x 64 floats) is gathered into LDS once per workgroup with 16-byte
+// buffer-to-LDS loads, already in the order the matrix instructions take it:
+// 1 KiB fragments (rows 16 R .. 16 R + 15, columns 16 v .. 16 v + 15) in which
+// lane ri + 16 g holds row 16 R + ri, columns 16 v + 4 g .. + 3.  Every
+// wavefront then reads its operands with linear, conflict-free 16-byte LDS
+// reads, and the two wavefronts that share key columns do not load them
+// twice.  Two 16 KiB buffers alternate, the next half tile's gather in flight
+// during the current half's matrix instructions (one barrier per half).  The
+// MFMA is fed Km as its first operand and Qm as its second, so it produces
+// the transposed tile: lane (ri, g) holds scores[i0 + ri][j0 + 4 g .. 4 g +
+// 3], one 16-byte store per 16 x 16 tile after the second half.  Rows and
+// column tiles past the last block read zeros and store nothing.  Measured at
+// the 5 s shape: 125 us with the operands pipelined through registers, 115 us
+// with whole key tiles in two 32 KiB buffers (two workgroups per CU), 103-108
+// us with half tiles (32 KiB of LDS and 126 registers: four workgroups per
+// CU); runs of 4 and 16 tiles were slower than 8 in both LDS forms.
 #ifndef H3F_SCORE_RUN
 #define H3F_SCORE_RUN 8
 #endif
 constexpr uint32_t kScoreRun = H3F_SCORE_RUN;  // column tiles per workgroup
-
-__device__ __forceinline__ void mfma_tile32_t(f32x4 (&acc)[2][2], const float (&A)[2][32],
-                                              const float (&B)[2][32]) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 32; ++kk) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(B[n][kk], A[m][kk], acc[m][n], 0, 0, 0);
-    }
-}
 
 // acc[m][n][e] = scores[i0 + 16 m + ri][j0 + 16 n + 4 g + e].  Stores go
 // through a buffer resource over the head's score matrix; an element outside
@@ -359,7 +346,8 @@ __device__ __forceinline__ void wait_own_gather() {
 
 template <int SB>
 __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
-    __shared__ u32x4 kbuf[2][kTileFrags * 64];
+    constexpr int HF = kTileFrags / 2;  // 1 KiB fragments per half key tile (64 of 128 columns)
+    __shared__ u32x4 kbuf[2][HF * 64];
     const uint32_t runs = (a.tiles + kScoreRun - 1) / kScoreRun;
     const uint32_t per_head = a.tiles * runs;
     const uint32_t w = xcd_linear(blockIdx.x, (uint32_t)a.heads * per_head);
@@ -380,45 +368,71 @@ __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
     const rsrc_t rk = make_rsrc(a.pooled + ((size_t)a.heads + h) * a.nb * kHeadDim, mat_bytes);
     const rsrc_t ro = make_rsrc(a.scores + (size_t)h * a.nb * a.nb, a.nb * a.nb * 4u);
 
-    // wavefront w gathers fragments 8 w .. 8 w + 7 of key tile t into buffer b;
-    // lane ri + 16 g of fragment f takes 16 bytes of row 16 (f / 8) + ri at
-    // column 16 (f mod 8) + 4 g (rows past nb read 0)
-    auto gather = [&](uint32_t t, int b) {
+    // step s = 2 t + hk: half hk of key tile t.  Wavefront w gathers fragments
+    // 4 w .. 4 w + 3 of it into buffer b; fragment f = 4 R + v' holds rows
+    // 16 R .. + 15 (rows past nb read 0), columns 64 hk + 16 v' .. + 15
+    auto gather = [&](int s, int b) {
+        const uint32_t t = (uint32_t)(s >> 1);
+        const uint32_t hk = (uint32_t)(s & 1);
 #pragma unroll
-        for (int f8 = 0; f8 < 8; ++f8) {
-            const int f = wave * 8 + f8;
-            const uint32_t row = jrun + t * kTile + 16u * (uint32_t)(f >> 3) + (uint32_t)ri;
-            const uint32_t off = row * (kHeadDim * 4u) + 64u * (uint32_t)(f & 7) + 16u * (uint32_t)g;
+        for (int f4 = 0; f4 < HF / 4; ++f4) {
+            const int f = wave * (HF / 4) + f4;
+            const uint32_t row = jrun + t * kTile + 16u * (uint32_t)(f >> 2) + (uint32_t)ri;
+            const uint32_t off = row * (kHeadDim * 4u) + 256u * hk + 64u * (uint32_t)(f & 3) + 16u * (uint32_t)g;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rk, (__attribute__((address_space(3))) void*)&kbuf[b][f * 64], 16, off, 0, 0,
                 kLoadReuse);
         }
     };
 
-    float A[2][32], B[2][32];
+    float A[2][32], B[2][16];
 #pragma unroll
     for (int m = 0; m < 2; ++m) load_row32(A[m], rq, i0 + 16 * m + ri, g);
     gather(0, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     f32x4 acc[2][2];
+    constexpr int NS = 2 * (int)kScoreRun;
 #pragma unroll
-    for (uint32_t t = 0; t < kScoreRun; ++t) {
-        if (t > 0) wait_own_gather<SB>();
-        __syncthreads();  // every gather of tile t is complete; buffer (t + 1) & 1 is free
+    for (int s = 0; s < NS; ++s) {
+        const int hk = s & 1;
+        if (s > 0) {
+            // this wavefront's gather of step s is complete; after a second half
+            // the tile's stores, issued after it, may still be in flight
+            if (hk == 0)
+                wait_own_gather<SB>();
+            else
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing was stored
+        }
+        __syncthreads();  // every gather of step s is complete; the other buffer is free
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                const u32x4 x = kbuf[t & 1][((rj + n) * 8 + v) * 64 + lane];
+            for (int v = 0; v < 4; ++v) {
+                const u32x4 x = kbuf[s & 1][((rj + n) * 4 + v) * 64 + lane];
                 B[n][4 * v + 0] = __uint_as_float(x[0]);
                 B[n][4 * v + 1] = __uint_as_float(x[1]);
                 B[n][4 * v + 2] = __uint_as_float(x[2]);
                 B[n][4 * v + 3] = __uint_as_float(x[3]);
             }
-        if (t + 1 < kScoreRun) gather(t + 1, (t + 1) & 1);
+        if (s + 1 < NS) gather(s + 1, (s + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_tile32_t(acc, A, B);
-        store_tile32_t<SB>(ro, a.nb, i0, jrun + t * kTile + (wave & 1) * kWaveTile, ri, g, acc);
+        if (hk == 0) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(B[n][kk], A[m][16 * hk + kk],
+                                                                     acc[m][n], 0, 0, 0);
+        if (hk == 1)
+            store_tile32_t<SB>(ro, a.nb, i0, jrun + (uint32_t)(s >> 1) * kTile + (wave & 1) * kWaveTile,
+                               ri, g, acc);
     }
 }
 
