@@ -346,7 +346,7 @@ __device__ __forceinline__ void wait_own_gather() {
 
 template <int SB>
 __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
-    constexpr int HF = kTileFrags / 2;  // 1 KiB fragments per half key tile (64 of 128 columns)
+    constexpr int HF = kTileFrags / 2;  // 1 KiB fragments per half key tile (64 columns)
     __shared__ u32x4 kbuf[2][HF * 64];
     const uint32_t runs = (a.tiles + kScoreRun - 1) / kScoreRun;
     const uint32_t per_head = a.tiles * runs;
@@ -378,7 +378,8 @@ __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
         for (int f4 = 0; f4 < HF / 4; ++f4) {
             const int f = wave * (HF / 4) + f4;
             const uint32_t row = jrun + t * kTile + 16u * (uint32_t)(f >> 2) + (uint32_t)ri;
-            const uint32_t off = row * (kHeadDim * 4u) + 256u * hk + 64u * (uint32_t)(f & 3) + 16u * (uint32_t)g;
+            const uint32_t off =
+                row * (kHeadDim * 4u) + 256u * hk + 64u * (uint32_t)(f & 3) + 16u * (uint32_t)g;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rk, (__attribute__((address_space(3))) void*)&kbuf[b][f * 64], 16, off, 0, 0,
                 kLoadReuse);
@@ -431,8 +432,9 @@ __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
                     acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(B[n][kk], A[m][16 * hk + kk],
                                                                      acc[m][n], 0, 0, 0);
         if (hk == 1)
-            store_tile32_t<SB>(ro, a.nb, i0, jrun + (uint32_t)(s >> 1) * kTile + (wave & 1) * kWaveTile,
-                               ri, g, acc);
+            store_tile32_t<SB>(ro, a.nb, i0,
+                               jrun + (uint32_t)(s >> 1) * kTile + (wave & 1) * kWaveTile, ri, g,
+                               acc);
     }
 }
 
