@@ -319,8 +319,11 @@ h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores,
  * heads <= 4096; H3F_ERR_UNSUPPORTED otherwise, and rows == 0 is rejected).
  * Errors: as h3f_qk_rmsnorm_rope3d; H3F_ERR_WORKSPACE for a missing,
  * misaligned or short workspace; H3F_ERR_ALIASING if it overlaps a tensor.
- * The block sums run in token order in fp32, so the means can differ from the
- * separate route's in the last bits.
+ * Each block sum is formed in fp32 in a fixed order: 16 wavefronts each add
+ * the block's 2-token chunks w, w + 16, w + 32, ... (w = 0..15) in order, and
+ * the 16 partial sums are then added in wavefront order.  The order depends
+ * only on the shape, so the means are the same run to run, but they can
+ * differ from the separate route's (which sums differently) in the last bits.
  */
 h3f_status_t h3f_qk_rmsnorm_rope3d_pool(void* q_out, int64_t q_out_row_stride,
                                         int64_t q_out_head_stride, void* k_out,

@@ -169,13 +169,30 @@ def _mod(v, hidden, name):
 
 
 def _rows_per_group(rows, groups, rows_per_group):
+    """Rows per modulation group.  The library reads group ceil(rows / rpg) - 1 as
+    its last one, so the tensors must hold at least that many groups."""
     if rows_per_group is not None:
-        return int(rows_per_group)
-    if groups == 1:
-        return max(rows, 1)
-    if rows % groups:
+        rpg = int(rows_per_group)
+        if rpg < 1:
+            raise ValueError("rows_per_group must be >= 1")
+    elif groups == 1:
+        rpg = max(rows, 1)
+    elif rows % groups:
         raise ValueError("rows_per_group is needed when rows is not a multiple of the group count")
-    return rows // groups
+    else:
+        rpg = rows // groups
+    if rows > 0 and -(-rows // rpg) > groups:
+        raise ValueError(f"{rows} rows at {rpg} rows per group need {-(-rows // rpg)} modulation "
+                         f"groups; the modulation tensors hold {groups}")
+    return rpg
+
+
+def _same_dtype(ref, name_ref, *named):
+    """Modulation vectors and LayerNorm weights are read in the type of the stream
+    tensor they act on."""
+    for t, n in named:
+        if t.dtype != ref.dtype:
+            raise TypeError(f"{n} must have {name_ref}'s dtype ({ref.dtype}), got {t.dtype}")
 
 
 # ---------------------------------------------------------------------------------
@@ -205,6 +222,7 @@ def h3f_adaln_modulate(y, x, shift, scale, eps: float = 1e-6, rows_per_group=Non
     g2, gs2 = _mod(scale, hidden, "scale")
     if (groups, gs) != (g2, gs2):
         raise ValueError("shift and scale must share shape and strides")
+    _same_dtype(x, "x", (shift, "shift"), (scale, "scale"))
     rpg = _rows_per_group(rows, groups, rows_per_group)
     _check("h3f_adaln_modulate", lib().h3f_adaln_modulate(
         _ptr(y), _dtype(y), ys, _ptr(x), _dtype(x), xs, _ptr(shift), _ptr(scale), gs, rpg, rows,
@@ -227,6 +245,7 @@ def h3f_adaln_affine_modulate(y, x, gamma, beta, shift, scale, eps: float = 1e-6
     g2, gs2 = _mod(scale, hidden, "scale")
     if (groups, gs) != (g2, gs2):
         raise ValueError("shift and scale must share shape and strides")
+    _same_dtype(x, "x", (shift, "shift"), (scale, "scale"), (gamma, "gamma"), (beta, "beta"))
     rpg = _rows_per_group(rows, groups, rows_per_group)
     _check("h3f_adaln_affine_modulate", lib().h3f_adaln_affine_modulate(
         _ptr(y), _dtype(y), ys, _ptr(x), _dtype(x), xs, _ptr(gamma), _ptr(beta), _ptr(shift),
@@ -242,6 +261,7 @@ def h3f_gated_residual(x, h, gate, rows_per_group=None, stream=None):
     if (hr, hh) != (rows, hidden):
         raise ValueError("h and x shapes differ")
     groups, gs = _mod(gate, hidden, "gate")
+    _same_dtype(x, "x", (gate, "gate"))
     rpg = _rows_per_group(rows, groups, rows_per_group)
     _check("h3f_gated_residual", lib().h3f_gated_residual(
         _ptr(x), _dtype(x), xs, _ptr(h), _dtype(h), hs, _ptr(gate), gs, rpg, rows, hidden,
@@ -273,14 +293,37 @@ def h3f_swiglu(out, a, b=None, stream=None):
 
 def make_rope(T, H, W, n_audio, split, theta=10000.0, token_offset=0, positions=None,
               pairing=H3F_ROPE_INTERLEAVED) -> Rope3D:
+    """Token grid and RoPE parameters.  `positions`, when given, is a contiguous int32
+    [rows, 3] GPU tensor of (t, h, w) per row; the returned struct keeps a reference
+    to it, and the QK calls check it against their rows and device."""
+    import torch
+
     r = Rope3D()
     r.T, r.H, r.W, r.n_audio = int(T), int(H), int(W), int(n_audio)
     r.d_t, r.d_h, r.d_w = (int(s) for s in split)
     r.pairing = int(pairing)
     r.theta = float(theta)
     r.token_offset = int(token_offset)
+    if positions is not None:
+        if (positions.dtype != torch.int32 or positions.dim() != 2 or positions.shape[1] != 3
+                or not positions.is_contiguous()):
+            raise ValueError("positions must be a contiguous int32 [rows, 3] tensor")
+        if not positions.is_cuda:
+            raise ValueError("positions must be a GPU tensor")
     r.positions = None if positions is None else positions.data_ptr()
+    r.positions_tensor = positions  # keeps the array alive as long as the struct
     return r
+
+
+def _check_rope(rope: Rope3D, rows: int, dev):
+    pos = getattr(rope, "positions_tensor", None)
+    if rope.positions and pos is None:
+        raise ValueError("rope.positions was set outside make_rope; pass positions to make_rope")
+    if pos is not None:
+        if pos.shape[0] < rows:
+            raise ValueError(f"rope positions hold {pos.shape[0]} rows; the call has {rows}")
+        if pos.device != dev:
+            raise ValueError("rope positions must be on the device of q and k")
 
 
 def _heads3d(t, name):
@@ -315,6 +358,7 @@ def h3f_qk_rmsnorm_rope3d_pool(q_out, k_out, q, k, q_weight, k_weight, rope: Rop
     gives for the same rows, heads, head_dim and block)."""
     dev = _dev(q_out, k_out, q, k, q_weight, k_weight, workspace)
     args = _qk_args(q_out, k_out, q, k, q_weight, k_weight)
+    _check_rope(rope, q.shape[0], dev)
     _check("h3f_qk_rmsnorm_rope3d_pool", lib().h3f_qk_rmsnorm_rope3d_pool(
         *args, eps, ctypes.byref(rope), block, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(dev, stream)))
@@ -360,6 +404,7 @@ def h3f_qk_rmsnorm_rope3d(q_out, k_out, q, k, q_weight, k_weight, rope: Rope3D,
     for t in (k, q_out, k_out, q_weight, k_weight):
         if _dtype(t) != dt:
             raise TypeError("all qk tensors must share one dtype")
+    _check_rope(rope, rows, dev)
     _check("h3f_qk_rmsnorm_rope3d", lib().h3f_qk_rmsnorm_rope3d(
         _ptr(q_out), qors, qohs, _ptr(k_out), kors, kohs, _ptr(q), qrs, qhs, _ptr(k), krs, khs,
         _ptr(q_weight), _ptr(k_weight), dt, rows, heads, head_dim, eps, ctypes.byref(rope),
@@ -380,6 +425,7 @@ def h3f_gated_residual_adaln(x, h, gate, shift, scale, y, eps: float = 1e-6,
     if len(set(shapes)) != 1:
         raise ValueError("gate, shift and scale must share shape and strides")
     groups, gs = shapes[0]
+    _same_dtype(x, "x", (gate, "gate"), (shift, "shift"), (scale, "scale"))
     rpg = _rows_per_group(rows, groups, rows_per_group)
     _check("h3f_gated_residual_adaln", lib().h3f_gated_residual_adaln(
         _ptr(x), _dtype(x), xs, _ptr(h), _dtype(h), hs, _ptr(gate), _ptr(shift), _ptr(scale), gs,
