@@ -357,6 +357,20 @@ h3f_status_t h3f_subblock_route_pooled(int32_t* kv_blocks, float* scores, int64_
  */
 h3f_status_t h3f_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 
+/*
+ * The two directions of the copy alone (measurement helpers, not operators):
+ * h3f_stream_read reads src[0:bytes) with 16-byte vector loads -- streaming
+ * (non-temporal) loads, or ordinary cached loads when `cached` is non-zero --
+ * and folds the words it loaded; it writes 4 bytes to `sink` (device, 16 bytes,
+ * 16-byte aligned) only if the fold hits a fixed 32-bit value, so in practice
+ * it stores nothing.  h3f_stream_fill writes the 32-bit `value` repeatedly over
+ * dst[0:bytes) with 16-byte streaming stores.  bytes must be a multiple of 16.
+ * Errors: NULL_POINTER, BAD_SHAPE, MISALIGNED; ALIASING if sink overlaps src.
+ */
+h3f_status_t h3f_stream_read(const void* src, int64_t bytes, int32_t cached, void* sink,
+                             void* stream);
+h3f_status_t h3f_stream_fill(void* dst, int64_t bytes, uint32_t value, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

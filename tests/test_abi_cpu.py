@@ -221,6 +221,23 @@ def test_positions_and_copy_validation():
     assert L.h3f_stream_copy(A(0), P(0x20000008), 64, None) == MISAL
 
 
+def test_stream_read_and_fill_validation():
+    # zero bytes is a no-op before any other check; the rest is rejected on the host
+    assert L.h3f_stream_read(None, 0, 0, None, None) == OK
+    assert L.h3f_stream_read(None, 16, 0, A(1), None) == NULLP
+    assert L.h3f_stream_read(A(0), 16, 0, None, None) == NULLP
+    assert L.h3f_stream_read(A(0), 17, 0, A(1), None) == SHAPE
+    assert L.h3f_stream_read(A(0), -16, 1, A(1), None) == SHAPE
+    assert L.h3f_stream_read(P(0x10000008), 64, 0, A(1), None) == MISAL
+    assert L.h3f_stream_read(A(0), 64, 0, P(0x20000008), None) == MISAL
+    # the sink inside the bytes read
+    assert L.h3f_stream_read(P(0x10000000), 64, 1, P(0x10000000 + 32), None) == ALIAS
+    assert L.h3f_stream_fill(None, 0, 7, None) == OK
+    assert L.h3f_stream_fill(None, 16, 7, None) == NULLP
+    assert L.h3f_stream_fill(A(0), 24, 7, None) == SHAPE
+    assert L.h3f_stream_fill(P(0x10000004), 32, 7, None) == MISAL
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     import torch
 

@@ -35,7 +35,8 @@ EXPORTS = [
     "h3f_gated_residual", "h3f_swiglu", "h3f_qk_rmsnorm_rope3d", "h3f_gated_residual_adaln",
     "h3f_stream_copy", "h3f_residual_l1_workspace_bytes", "h3f_residual_l1",
     "h3f_subblock_plan", "h3f_subblock_route", "h3f_adaln_affine_modulate",
-    "h3f_qk_rmsnorm_rope3d_pool", "h3f_subblock_route_pooled",
+    "h3f_qk_rmsnorm_rope3d_pool", "h3f_subblock_route_pooled", "h3f_stream_read",
+    "h3f_stream_fill",
 ]
 
 
@@ -84,6 +85,8 @@ def lib():
         L.h3f_gated_residual_adaln.argtypes = [p, st, i64, p, st, i64, p, p, p, i64, i64, p, st,
                                                i64, i64, i64, f, p]
         L.h3f_stream_copy.argtypes = [p, p, i64, p]
+        L.h3f_stream_read.argtypes = [p, i64, i32, p, p]
+        L.h3f_stream_fill.argtypes = [p, i64, ctypes.c_uint32, p]
         L.h3f_residual_l1.argtypes = [p, p, i64, p, i64, st, i64, i64, p, ctypes.c_size_t, p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = st
@@ -511,4 +514,27 @@ def h3f_stream_copy(dst, src, stream=None):
         raise ValueError("dst and src must be contiguous with equal byte sizes")
     _check("h3f_stream_copy", lib().h3f_stream_copy(_ptr(dst), _ptr(src), nb,
                                                     _stream(dev, stream)))
+    return dst
+
+
+def h3f_stream_read(src, sink, cached: bool = False, stream=None):
+    """Read all of src (contiguous) once (measurement helper); sink: >= 16-byte
+    GPU tensor that is written only if the loaded data folds to a fixed value."""
+    dev = _dev(src, sink)
+    if not (src.is_contiguous() and sink.is_contiguous()) or sink.numel() * sink.element_size() < 16:
+        raise ValueError("src must be contiguous and sink a contiguous tensor of >= 16 bytes")
+    _check("h3f_stream_read", lib().h3f_stream_read(
+        _ptr(src), src.numel() * src.element_size(), 1 if cached else 0, _ptr(sink),
+        _stream(dev, stream)))
+    return src
+
+
+def h3f_stream_fill(dst, value: int = 0, stream=None):
+    """Write the 32-bit pattern `value` over all of dst (contiguous; measurement helper)."""
+    dev = _dev(dst)
+    if not dst.is_contiguous():
+        raise ValueError("dst must be contiguous")
+    _check("h3f_stream_fill", lib().h3f_stream_fill(
+        _ptr(dst), dst.numel() * dst.element_size(), int(value) & 0xFFFFFFFF,
+        _stream(dev, stream)))
     return dst

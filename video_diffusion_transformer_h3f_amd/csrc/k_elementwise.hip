@@ -1,5 +1,5 @@
 // k_elementwise.hip -- streaming operators of libh3fused: gated residual,
-// SwiGLU, and the streaming-copy measurement helper.
+// SwiGLU, and the streaming measurement helpers (copy, read-only, fill).
 //
 // Design (gfx950): the [rows, cols] problem is flattened into row-major
 // vector chunks of VEC elements (one 16-byte quad for bf16, one or two for
@@ -161,6 +161,42 @@ stream_copy_kernel(char* __restrict__ dst, const char* __restrict__ src, uint64_
     for (int u = 0; u < kUnroll; ++u) v[u] = buf_ld<kLoadStream>(rs, 16u * (u * kBlock + threadIdx.x));
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) buf_st<kStoreStream>(rd, 16u * (u * kBlock + threadIdx.x), v[u]);
+}
+
+// ---------------------------------------------------------------------------
+// Read-only and write-only streams (measurement helpers): one direction of the
+// copy alone, in 256-thread workgroups.  Reads keep 8 chunks per lane in flight
+// (reads alone stream well at that depth); the loaded words are folded with XOR
+// and written only if they equal `magic`, so the loads cannot be dropped yet
+// nothing is stored in practice.  The fill stores one chunk per lane: measured
+// on MI355X over 1.28 GB, 7.07 TB/s against 5.68 with 8 chunks per lane and 4.8
+// with 64-thread workgroups (workgroup dispatch rate).
+// ---------------------------------------------------------------------------
+constexpr int kDirBlock = 256;
+constexpr int kDirUnroll = 8;
+constexpr uint64_t kDirTileBytes = (uint64_t)kDirBlock * kDirUnroll * 16;
+constexpr uint64_t kFillTileBytes = (uint64_t)kDirBlock * 16;
+
+template <int AUX>
+__global__ void __launch_bounds__(kDirBlock)
+stream_read_kernel(const char* __restrict__ src, uint64_t bytes, unsigned magic,
+                   unsigned* __restrict__ sink) {
+    const uint64_t t0 = (uint64_t)blockIdx.x * kDirTileBytes;
+    const uint64_t left = bytes - t0;
+    const rsrc_t rs = make_rsrc(src + t0, left < kDirTileBytes ? (uint32_t)left : (uint32_t)kDirTileBytes);
+    u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < kDirUnroll; ++u) acc ^= buf_ld<AUX>(rs, 16u * (u * kDirBlock + threadIdx.x));
+    const unsigned v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (v == magic) sink[0] = v;
+}
+
+__global__ void __launch_bounds__(kDirBlock)
+stream_fill_kernel(char* __restrict__ dst, uint64_t bytes, unsigned value) {
+    const uint64_t t0 = (uint64_t)blockIdx.x * kFillTileBytes;
+    const uint64_t left = bytes - t0;
+    const rsrc_t rd = make_rsrc(dst + t0, left < kFillTileBytes ? (uint32_t)left : (uint32_t)kFillTileBytes);
+    buf_st<kStoreStream>(rd, 16u * threadIdx.x, u32x4{value, value, value, value});
 }
 
 inline unsigned blocks_for(int64_t chunks) {
@@ -330,5 +366,41 @@ extern "C" h3f_status_t h3f_stream_copy(void* dst, const void* src, int64_t byte
     hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
                        static_cast<hipStream_t>(stream), static_cast<char*>(dst),
                        static_cast<const char*>(src), (uint64_t)bytes);
+    return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
+}
+
+extern "C" h3f_status_t h3f_stream_read(const void* src, int64_t bytes, int32_t cached,
+                                        void* sink, void* stream) {
+    if (bytes == 0) return H3F_OK;
+    if (!src || !sink) return H3F_ERR_NULL_POINTER;
+    if (bytes < 0 || bytes % 16) return H3F_ERR_BAD_SHAPE;
+    if (!aligned16(src) || !aligned16(sink)) return H3F_ERR_MISALIGNED;
+    if (!disjoint(region2d(sink, 1, 0, 16, 1), region2d(src, 1, 0, bytes, 1))) return H3F_ERR_ALIASING;
+    const uint64_t blocks = ((uint64_t)bytes + kDirTileBytes - 1) / kDirTileBytes;
+    if (blocks > 0xffffffffull) return H3F_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // a value no fold of real data is expected to reach; a hit writes 4 bytes to sink
+    const unsigned magic = 0x9e3779b9u;
+    if (cached)
+        hipLaunchKernelGGL(stream_read_kernel<kLoadReuse>, dim3((unsigned)blocks), dim3(kDirBlock), 0, st,
+                           static_cast<const char*>(src), (uint64_t)bytes, magic,
+                           static_cast<unsigned*>(sink));
+    else
+        hipLaunchKernelGGL(stream_read_kernel<kLoadStream>, dim3((unsigned)blocks), dim3(kDirBlock), 0, st,
+                           static_cast<const char*>(src), (uint64_t)bytes, magic,
+                           static_cast<unsigned*>(sink));
+    return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
+}
+
+extern "C" h3f_status_t h3f_stream_fill(void* dst, int64_t bytes, uint32_t value, void* stream) {
+    if (bytes == 0) return H3F_OK;
+    if (!dst) return H3F_ERR_NULL_POINTER;
+    if (bytes < 0 || bytes % 16) return H3F_ERR_BAD_SHAPE;
+    if (!aligned16(dst)) return H3F_ERR_MISALIGNED;
+    const uint64_t blocks = ((uint64_t)bytes + kFillTileBytes - 1) / kFillTileBytes;
+    if (blocks > 0xffffffffull) return H3F_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(stream_fill_kernel, dim3((unsigned)blocks), dim3(kDirBlock), 0,
+                       static_cast<hipStream_t>(stream), static_cast<char*>(dst), (uint64_t)bytes,
+                       value);
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }
