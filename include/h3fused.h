@@ -247,6 +247,31 @@ h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cur_row_strid
                              size_t workspace_bytes, void* stream);
 
 /*
+ * h3f_residual_l1 for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and result, bit for bit, with the per-workgroup partial sums kept in
+ * a device array the library owns instead of a caller workspace.  The call
+ * itself allocates nothing and frees nothing.
+ *   Limit: the array holds h3f_residual_l1_noalloc_max_bytes() bytes (4 MiB);
+ *   a call whose h3f_residual_l1_workspace_bytes(rows, hidden, dtype) is larger
+ *   is rejected with H3F_ERR_WORKSPACE (bf16 at hidden 5120: up to 838,860
+ *   rows).  Each GPU the library runs on holds its own copy of the array until
+ *   the process ends; its address is looked up once per device, on the first
+ *   call with that device current (H3F_ERR_LAUNCH if the lookup fails).
+ *   Sharing: every call on one GPU uses that GPU's array, which keeps the last
+ *   call's partial sums (each call writes all the sums it reads, so no clearing
+ *   is needed).  Calls that may run concurrently on one GPU (other streams,
+ *   other host threads without ordering) race on the array and must not
+ *   overlap; calls ordered on one stream are safe.
+ * Arguments, result and other errors as h3f_residual_l1.
+ */
+size_t h3f_residual_l1_noalloc_max_bytes(void);
+h3f_status_t h3f_residual_l1_noalloc(double* out, const void* cur, int64_t cur_row_stride,
+                                     const void* prev, int64_t prev_row_stride,
+                                     h3f_dtype_t dtype, int64_t rows, int64_t hidden,
+                                     void* stream);
+
+/*
  * Block-sparse attention router (SubBlock).  The report page (section "Só com
  * três camadas…", SubBlock paragraph) describes a block router that, from the
  * tenth denoising step on, cuts the key/value blocks each attention

@@ -36,7 +36,7 @@ EXPORTS = [
     "h3f_stream_copy", "h3f_residual_l1_workspace_bytes", "h3f_residual_l1",
     "h3f_subblock_plan", "h3f_subblock_route", "h3f_adaln_affine_modulate",
     "h3f_qk_rmsnorm_rope3d_pool", "h3f_subblock_route_pooled", "h3f_stream_read",
-    "h3f_stream_fill",
+    "h3f_stream_fill", "h3f_residual_l1_noalloc", "h3f_residual_l1_noalloc_max_bytes",
 ]
 
 
@@ -88,8 +88,11 @@ def lib():
         L.h3f_stream_read.argtypes = [p, i64, i32, p, p]
         L.h3f_stream_fill.argtypes = [p, i64, ctypes.c_uint32, p]
         L.h3f_residual_l1.argtypes = [p, p, i64, p, i64, st, i64, i64, p, ctypes.c_size_t, p]
+        L.h3f_residual_l1_noalloc.argtypes = [p, p, i64, p, i64, st, i64, i64, p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = st
+        L.h3f_residual_l1_noalloc_max_bytes.argtypes = []
+        L.h3f_residual_l1_noalloc_max_bytes.restype = ctypes.c_size_t
         L.h3f_residual_l1_workspace_bytes.argtypes = [i64, i64, st]
         L.h3f_residual_l1_workspace_bytes.restype = ctypes.c_size_t
         L.h3f_subblock_plan.argtypes = [i64, i32, i32, i32, ctypes.c_double, i32,
@@ -464,6 +467,31 @@ def h3f_residual_l1(out, cur, prev, workspace=None, stream=None):
         _ptr(out), _ptr(cur), cs, _ptr(prev), ps, _dtype(cur), rows, hidden, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(dev, stream)))
     return out
+
+
+def h3f_residual_l1_noalloc(out, cur, prev, stream=None):
+    """h3f_residual_l1 with the library's own device scratch instead of a workspace
+    (no allocation of any kind; for callers that cannot allocate).  Calls that
+    overlap on one GPU share that scratch and race."""
+    import torch
+
+    dev = _dev(out, cur, prev)
+    if out.dtype != torch.float64 or out.numel() < 3 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float64 tensor of >= 3 elements")
+    rows, hidden, cs = _rows2d(cur, "cur")
+    pr, ph, ps = _rows2d(prev, "prev")
+    if (pr, ph) != (rows, hidden) or cur.dtype != prev.dtype:
+        raise ValueError("cur and prev must share shape and dtype")
+    _check("h3f_residual_l1_noalloc", lib().h3f_residual_l1_noalloc(
+        _ptr(out), _ptr(cur), cs, _ptr(prev), ps, _dtype(cur), rows, hidden,
+        _stream(dev, stream)))
+    return out
+
+
+def h3f_residual_l1_noalloc_max_bytes() -> int:
+    """Bytes of the device scratch behind h3f_residual_l1_noalloc; calls whose
+    h3f_residual_l1_workspace_bytes() exceeds it are rejected."""
+    return int(lib().h3f_residual_l1_noalloc_max_bytes())
 
 
 def h3f_subblock_plan(rows: int, heads: int, head_dim: int, block: int, sparsity: float,

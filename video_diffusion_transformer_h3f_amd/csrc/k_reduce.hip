@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "h3f_device.hpp"
 #include "h3f_validate.hpp"
@@ -183,10 +184,13 @@ extern "C" size_t h3f_residual_l1_workspace_bytes(int64_t rows, int64_t hidden,
     return (size_t)n_partials(rows, hidden / V) * 2 * sizeof(double);
 }
 
-extern "C" h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cur_row_stride,
-                                        const void* prev, int64_t prev_row_stride,
-                                        h3f_dtype_t dtype, int64_t rows, int64_t hidden,
-                                        void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Checks shared by the workspace and the no-allocation entry points; on success
+// *cs / *ps hold the row strides the kernels use.
+h3f_status_t l1_validate(const double* out, const void* cur, int64_t cur_row_stride,
+                         const void* prev, int64_t prev_row_stride, h3f_dtype_t dtype,
+                         int64_t rows, int64_t hidden, int64_t* cs_out, int64_t* ps_out) {
     if (!out) return H3F_ERR_NULL_POINTER;
     if (rows < 0 || hidden <= 0) return H3F_ERR_BAD_SHAPE;
     if (rows == 0) return H3F_ERR_BAD_SHAPE;  // the relative difference needs at least one element
@@ -207,18 +211,90 @@ extern "C" h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cu
     if (!rows_separate(rc) || !rows_separate(rp)) return H3F_ERR_BAD_STRIDE;
     if (!tile_fits2(hidden / V, cs * e, hidden * e) || !tile_fits2(hidden / V, ps * e, hidden * e))
         return H3F_ERR_UNSUPPORTED;
-    const size_t need = h3f_residual_l1_workspace_bytes(rows, hidden, dtype);
-    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return H3F_ERR_WORKSPACE;
-    const Region rw = region2d(workspace, 1, 0, (int64_t)need, 1);
     const Region ro = region2d(out, 1, 0, 3 * sizeof(double), 1);
-    if (!disjoint(rw, rc) || !disjoint(rw, rp) || !disjoint(ro, rc) || !disjoint(ro, rp) ||
-        !disjoint(ro, rw))
-        return H3F_ERR_ALIASING;
+    if (!disjoint(ro, rc) || !disjoint(ro, rp)) return H3F_ERR_ALIASING;
+    *cs_out = cs;
+    *ps_out = ps;
+    return H3F_OK;
+}
+
+h3f_status_t l1_launch(double* out, const void* cur, int64_t cs, const void* prev, int64_t ps,
+                       h3f_dtype_t dtype, int64_t rows, int64_t hidden, double* partial,
+                       void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    double* partial = static_cast<double*>(workspace);
     const hipError_t err =
         dtype == H3F_BF16
             ? launch_l1<__bf16, 8>(out, cur, cs, prev, ps, rows, hidden, partial, st)
             : launch_l1<float, 4>(out, cur, cs, prev, ps, rows, hidden, partial, st);
     return err == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch for h3f_residual_l1_noalloc: the per-workgroup partial
+// sums live in this file-scope device array instead of a caller workspace.
+// Each GPU the library runs on holds its own copy until the process ends.  Host
+// code never passes the array's name to a kernel or a copy (on the host it is
+// only a stand-in symbol): the device address is taken once per device with
+// hipGetSymbolAddress, with that device current, and that address is used.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(4) << 20;  // 262,144 (sum, sum) pairs
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, or nullptr on failure.
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cur_row_stride,
+                                        const void* prev, int64_t prev_row_stride,
+                                        h3f_dtype_t dtype, int64_t rows, int64_t hidden,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    int64_t cs = 0, ps = 0;
+    const h3f_status_t s = l1_validate(out, cur, cur_row_stride, prev, prev_row_stride, dtype,
+                                       rows, hidden, &cs, &ps);
+    if (s != H3F_OK) return s;
+    const int e = dtype_bytes(dtype);
+    const size_t need = h3f_residual_l1_workspace_bytes(rows, hidden, dtype);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return H3F_ERR_WORKSPACE;
+    const Region rw = region2d(workspace, 1, 0, (int64_t)need, 1);
+    const Region ro = region2d(out, 1, 0, 3 * sizeof(double), 1);
+    if (!disjoint(rw, region2d(cur, rows, cs, hidden, e)) ||
+        !disjoint(rw, region2d(prev, rows, ps, hidden, e)) || !disjoint(ro, rw))
+        return H3F_ERR_ALIASING;
+    return l1_launch(out, cur, cs, prev, ps, dtype, rows, hidden, static_cast<double*>(workspace),
+                     stream);
+}
+
+extern "C" size_t h3f_residual_l1_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" h3f_status_t h3f_residual_l1_noalloc(double* out, const void* cur,
+                                                int64_t cur_row_stride, const void* prev,
+                                                int64_t prev_row_stride, h3f_dtype_t dtype,
+                                                int64_t rows, int64_t hidden, void* stream) {
+    int64_t cs = 0, ps = 0;
+    const h3f_status_t s = l1_validate(out, cur, cur_row_stride, prev, prev_row_stride, dtype,
+                                       rows, hidden, &cs, &ps);
+    if (s != H3F_OK) return s;
+    if (h3f_residual_l1_workspace_bytes(rows, hidden, dtype) > kScratchBytes)
+        return H3F_ERR_WORKSPACE;  // more partial sums than the library's scratch holds
+    void* partial = scratch_for_current_device();
+    if (!partial) return H3F_ERR_LAUNCH;
+    // every partial pair is written by the first kernel before the second reads it,
+    // so the scratch needs no clearing between calls
+    return l1_launch(out, cur, cs, prev, ps, dtype, rows, hidden, static_cast<double*>(partial),
+                     stream);
 }
