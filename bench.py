@@ -12,10 +12,20 @@ Inputs are generated on the device before timing.  The reported value is the
 step's algorithmic bytes (each input element read once, each output element
 written once) divided by the step time: achieved HBM GB/s.  Per-operator
 durations come from HIP events recorded around every launch on the stream the
-kernels run on.  The CPU oracle is timed on a bounded sample of the same
-workload (rank 0) as a baseline.  Outside the step, `extra_ops` times the
-step-reuse residual difference and the block-sparse attention router on the
-same shape.
+kernels run on.
+
+Beside the headline step the default run also times, each outside the
+headline's timed region:
+  * bandwidth references on 2 GiB buffers: the library's streaming copy,
+    hipMemcpyDtoD (torch copy_), a read-only and a write-only stream;
+  * the same block with each gated residual fused into the AdaLN that follows
+    it (four calls per step);
+  * the step-reuse residual difference and the block-sparse attention router;
+  * the 10 s fp32-residual packed-qkv block epilogue chain, 50 steps.
+After all timing, the oracle leg runs on the host: the CPU baseline (the oracle
+timed on a bounded sample of the workload) and the check of every timed step's
+outputs against the oracle on sampled rows (per-operator max |err| / tol; the
+run exits non-zero if any exceeds 1).
 
 On the sweep shapes (tensors of a few hundred MB, comparable to the 256 MB
 Infinity Cache) a 1 GiB scratch buffer is written before every timed launch
@@ -23,7 +33,7 @@ Infinity Cache) a 1 GiB scratch buffer is written before every timed launch
 the sum of the launch times.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5s|10s|chain10s|sweepD]
-                       [--fused] [--no-cpu-baseline] [--seed S] [--flush-mb M]
+                       [--fused] [--no-extras] [--no-cpu-baseline] [--seed S] [--flush-mb M]
 """
 from __future__ import annotations
 
@@ -47,6 +57,8 @@ for _D, _F in ((3072, 8320), (4096, 11008), (5120, 13824), (6144, 16640)):
     GRIDS[f"sweep{_D}"] = dict(T=8, H=48, W=84, A=512, D=_D, heads=_D // 128, Dh=128,
                                split=(32, 48, 48), F=_F)
 
+CHAIN_STEPS = 50  # the chain workload's step count (one DiT block epilogue per denoising step)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -56,6 +68,9 @@ def parse():
     ap.add_argument("--workload", default="5s", choices=sorted(GRIDS) + ["chain10s"])
     ap.add_argument("--fused", action="store_true",
                     help="fuse each gated residual with the AdaLN that follows it")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the bandwidth references and the headline step (no "
+                         "extra ops, other block form or chain)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32768,
                     help="rows of the workload the oracle is timed on")
@@ -66,6 +81,10 @@ def parse():
                          "the sweep shapes, whose tensors are comparable to the cache; 0 "
                          "otherwise)")
     return ap.parse_args()
+
+
+def n_tokens(c):
+    return c["T"] * c["H"] * c["W"] + c["A"]
 
 
 def op_bytes(name, N, c, x_bytes=2):
@@ -153,7 +172,7 @@ def build_inputs(c, N, torch, h3gen, dev, chain=False, seed=0):
 
 
 def make_step(h3, t, rope, fused):
-    """The six fused calls of one DiT block, each tagged with its operator name."""
+    """The fused calls of one DiT block, each tagged with its operator name."""
     if not fused:
         return [
             ("adaln", lambda: h3.h3f_adaln_modulate(t["y"], t["x"], t["shift"], t["scale"])),
@@ -175,6 +194,198 @@ def make_step(h3, t, rope, fused):
             t["x"], t["h"], t["gate"], t["shift2"], t["scale2"], t["y"])),
         ("swiglu", lambda: h3.h3f_swiglu(t["act"], t["gate_up"])),
     ]
+
+
+def time_step(torch, step, K, W, flush=None):
+    """W untimed warmup steps, then K timed steps with an event pair around every
+    launch (consecutive launches share their boundary event unless a flush runs
+    between them).  Returns (ms per step, {op: [launch ms]}, wall seconds)."""
+    for _ in range(W):
+        for _, fn in step:
+            fn()
+    torch.cuda.synchronize()
+    n_ops = len(step)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_ops)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(K):
+        for i, (_, fn) in enumerate(step):
+            if flush is not None:
+                flush()
+            if flush is not None or i == 0:
+                ev[s][2 * i].record()
+            fn()
+            ev[s][2 * i + 1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    def launch_ms(s, i):
+        first = ev[s][2 * i] if (flush is not None or i == 0) else ev[s][2 * i - 1]
+        return first.elapsed_time(ev[s][2 * i + 1])
+
+    per_op_all = {}
+    for s in range(K):
+        for i, (name, _) in enumerate(step):
+            per_op_all.setdefault(name, []).append(launch_ms(s, i))
+    if flush is None:
+        ms_per_step = start.elapsed_time(stop) / K
+    else:  # the flushes between launches are not part of a step
+        ms_per_step = sum(launch_ms(s, i) for s in range(K) for i in range(n_ops)) / K
+    return ms_per_step, per_op_all, wall
+
+
+def per_op_table(per_op_all, N, c, x_bytes, best_copy):
+    per_op = {}
+    for name, ts in per_op_all.items():
+        avg = sum(ts) / len(ts)
+        b = op_bytes(name, N, c, x_bytes)
+        st = sorted(ts)
+        gbps = b / (avg * 1e-3) / 1e9
+        per_op[name] = {"avg_ms": round(avg, 4), "median_ms": round(st[len(st) // 2], 4),
+                        "min_ms": round(st[0], 4), "launches": len(st), "bytes": b,
+                        "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                        "frac_of_best_copy": round(gbps / best_copy, 4) if best_copy else None}
+    return per_op
+
+
+def measure_references(torch, h3, dev):
+    """Bandwidth references on 2 GiB buffers (10 launches each after 3 warmups):
+    the library's streaming copy, hipMemcpyDtoD (torch copy_ of a contiguous
+    device tensor), a read-only stream (streaming and cached loads) and a
+    write-only stream."""
+    nb = 2 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    h3.h3f_stream_fill(src, 0x3F803F80)
+
+    def rate(fn, nbytes):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return round(10 * nbytes / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+
+    ref = {
+        "stream_copy_GBps": rate(lambda: h3.h3f_stream_copy(dst, src), 2 * nb),
+        "hipMemcpyDtoD_GBps": rate(lambda: dst.copy_(src), 2 * nb),
+        "read_only_GBps": rate(lambda: h3.h3f_stream_read(src, sink), nb),
+        "read_only_cached_GBps": rate(lambda: h3.h3f_stream_read(src, sink, cached=True), nb),
+        "write_only_GBps": rate(lambda: h3.h3f_stream_fill(dst, 0x3F803F80), nb),
+    }
+    ref["best_copy_GBps"] = max(ref["stream_copy_GBps"], ref["hipMemcpyDtoD_GBps"])
+    ref["note"] = ("2 GiB each way; copies count read + write bytes, the one-direction "
+                   "streams their own bytes")
+    del src, dst, sink
+    return ref
+
+
+def block_workload(args, torch, h3, h3gen, dev, c, chain, fused, K, W, best_copy, flush=None):
+    """Time K block steps (after W warmup steps) at grid c and fetch the sampled
+    output rows for the oracle check.  Returns (result dict, fetched rows, idx)."""
+    from bench_check import fetch_rows, sample_rows
+
+    N = n_tokens(c)
+    x_bytes = 4 if chain else 2
+    t = build_inputs(c, N, torch, h3gen, dev, chain=chain, seed=args.seed)
+    rope = h3.make_rope(c["T"], c["H"], c["W"], c["A"], c["split"])
+    step = make_step(h3, t, rope, fused)
+    ms_per_step, per_op_all, wall = time_step(torch, step, K, W, flush)
+    step_bytes = sum(op_bytes(name, N, c, x_bytes) for name, _ in step)
+    idx = sample_rows(N, N - c["A"])
+    got = fetch_rows(t, idx)
+    res = {
+        "value_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "ms_per_step": round(ms_per_step, 4),
+        "steps": K, "warmup": W, "step_bytes": step_bytes,
+        "per_op": per_op_table(per_op_all, N, c, x_bytes, best_copy),
+        "wall_s_timed_region": round(wall, 4),
+    }
+    return res, got, idx, t, rope
+
+
+def extra_ops_5s(args, torch, h3, h3gen, dev, c, t, rope, K, per_op):
+    """Step-reuse residual difference and the block-sparse attention router,
+    each timed on its own (a block runs them at most once per step)."""
+    N = n_tokens(c)
+    out = {}
+
+    def time_calls(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    x_prev = torch.empty_like(t["x"])
+    h3gen.fill_device(x_prev, "x_prev", seed=args.seed)
+    l1_out = torch.zeros(3, dtype=torch.float64, device=dev)
+    ws = torch.empty(max(16, h3.h3f_residual_l1_workspace_bytes(N, c["D"], t["x"].dtype)),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        h3.h3f_residual_l1(l1_out, t["x"], x_prev, ws)
+    torch.cuda.synchronize()
+    avg = time_calls(lambda: h3.h3f_residual_l1(l1_out, t["x"], x_prev, ws), K)
+    b = 2 * N * c["D"] * 2
+    out["residual_l1"] = {"avg_ms": round(avg, 4), "bytes": b,
+                          "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+                          "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    del x_prev, ws
+
+    # router on the step's post-RoPE q / k (what attention reads), blocks of 128
+    # tokens, sparsity 0.8, a routed step
+    blk, sp = 128, 0.8
+    nb, keep, need = h3.h3f_subblock_plan(N, c["heads"], c["Dh"], blk, sp, 10)
+    kv = torch.empty(c["heads"], nb, keep, dtype=torch.int32, device=dev)
+    sc = torch.empty(c["heads"], nb, nb, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        h3.h3f_subblock_route(kv, sc, t["q_out"], t["k_out"], blk, sp, 10, ws)
+    torch.cuda.synchronize()
+    avg = time_calls(lambda: h3.h3f_subblock_route(kv, sc, t["q_out"], t["k_out"], blk, sp,
+                                                   10, ws), K)
+    b = router_bytes(N, c, nb, keep)
+    out["subblock_route"] = {
+        "avg_ms": round(avg, 4), "bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+        "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "block": blk, "sparsity": sp, "n_blocks": nb, "keep": keep,
+        "score_flops": 2 * c["heads"] * nb * nb * c["Dh"]}
+
+    # a routed step with the router's pooling fused into the QK operator: the QK
+    # call that also writes the block means, then the route from them
+    def qk_pool():
+        h3.h3f_qk_rmsnorm_rope3d_pool(t["q_out"], t["k_out"], t["q"], t["k"], t["q_weight"],
+                                      t["k_weight"], rope, blk, ws)
+
+    def route_pooled():
+        h3.h3f_subblock_route_pooled(kv, sc, N, c["heads"], blk, sp, 10, ws)
+
+    for _ in range(3):
+        qk_pool()
+        route_pooled()
+    torch.cuda.synchronize()
+    a_qp = time_calls(qk_pool, K)
+    a_rp = time_calls(route_pooled, K)
+    b_qp = op_bytes("qk", N, c) + 2 * c["heads"] * nb * c["Dh"] * 4
+    b_rp = c["heads"] * nb * nb * 4 + c["heads"] * nb * keep * 4 + 2 * c["heads"] * nb * c["Dh"] * 4
+    out["qk_rmsnorm_rope3d_pool"] = {
+        "avg_ms": round(a_qp, 4), "bytes": b_qp, "GBps": round(b_qp / (a_qp * 1e-3) / 1e9, 1),
+        "frac_of_peak": round(b_qp / (a_qp * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    out["subblock_route_pooled"] = {
+        "avg_ms": round(a_rp, 4), "bytes": b_rp, "GBps": round(b_rp / (a_rp * 1e-3) / 1e9, 1)}
+    out["routed_qk_step_ms"] = {
+        "separate": round(per_op["qk"]["avg_ms"] + avg, 4), "fused": round(a_qp + a_rp, 4)}
+    del kv, sc, ws
+    return out
 
 
 def cpu_baseline(c, rows, x_bytes, min_seconds=10.0, seed=0):
@@ -250,188 +461,85 @@ def main():
     import h3gen
     import video_diffusion_transformer_h3f_amd as h3
 
+    sys.path.insert(0, os.path.join(ROOT, "tests"))  # the output check (oracle leg)
+
     h3.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     chain = args.workload == "chain10s"
     c = GRIDS["10s" if chain else args.workload]
-    N = c["T"] * c["H"] * c["W"] + c["A"]
+    N = n_tokens(c)
     x_bytes = 4 if chain else 2
-    t = build_inputs(c, N, torch, h3gen, dev, chain=chain, seed=args.seed)
+    extras = not args.no_extras
     flush_mb = args.flush_mb if args.flush_mb >= 0 else (
         1024 if args.workload.startswith("sweep") else 0)
     scratch = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev) if flush_mb else None
     flush = (lambda: scratch.fill_(1)) if flush_mb else None
+    if chain and args.steps == 30:
+        args.steps = CHAIN_STEPS
 
-    def time_calls(fn, reps):
-        """Average ms of fn over reps launches: back to back, or each after a flush
-        with its own event pair (the flush is outside the timed interval)."""
-        if flush is None:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(reps):
-                fn()
-            b.record()
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) / reps
-        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(reps)]
-        for a, b in pairs:
-            flush()
-            a.record()
-            fn()
-            b.record()
-        torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in pairs) / reps
-    rope = h3.make_rope(c["T"], c["H"], c["W"], c["A"], c["split"])
-    step = make_step(h3, t, rope, args.fused)
-    if chain:
-        args.steps = 50 if args.steps == 30 else args.steps
+    refs = measure_references(torch, h3, dev)
+    best_copy = refs["best_copy_GBps"]
+    checks = []  # (label, rows, idx, grid, steps run, fused, chain)
 
-    # copy ceiling (untimed for the metric): 2 GiB -> 2 GiB
-    cp_src = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
-    cp_dst = torch.empty_like(cp_src)
-    for _ in range(3):
-        h3.h3f_stream_copy(cp_dst, cp_src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        h3.h3f_stream_copy(cp_dst, cp_src)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 10 * 2 * cp_src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del cp_src, cp_dst
+    # ---- the headline step ----
+    head, got, idx, t, rope = block_workload(args, torch, h3, h3gen, dev, c, chain, args.fused,
+                                             args.steps, args.warmup, best_copy, flush)
+    checks.append(("headline", got, idx, c, args.warmup + args.steps, args.fused, chain))
+    per_op = head["per_op"]
 
-    for _ in range(args.warmup):
-        for _, fn in step:
-            fn()
-    torch.cuda.synchronize()
+    extra_ops, extra_workloads = {}, {}
+    if extras and args.workload == "5s" and not args.fused:
+        extra_ops = extra_ops_5s(args, torch, h3, h3gen, dev, c, t, rope, args.steps, per_op)
+    del t
+    torch.cuda.empty_cache()
+    if extras and args.workload == "5s":
+        # the other form of the same block: gated residual fused into the next AdaLN
+        # (or, when the headline is the fused block, the six separate calls)
+        other = not args.fused
+        res, got2, idx2, t, _ = block_workload(args, torch, h3, h3gen, dev, c, False, other,
+                                               args.steps, args.warmup, best_copy)
+        del t
+        torch.cuda.empty_cache()
+        extra_workloads["fused_block_5s" if other else "separate_block_5s"] = res
+        checks.append(("fused_block_5s" if other else "separate_block_5s", got2, idx2, c,
+                       args.warmup + args.steps, other, False))
+        # the 10 s fp32-residual packed-qkv epilogue chain (6 calls per step)
+        c10 = GRIDS["10s"]
+        res, got3, idx3, t, _ = block_workload(args, torch, h3, h3gen, dev, c10, True, False,
+                                               CHAIN_STEPS, args.warmup, best_copy)
+        del t
+        torch.cuda.empty_cache()
+        res["note"] = ("10 s shape, fp32 residual stream and modulation, bf16 activations, "
+                       "q/k read strided from a packed [tokens, 3, 40, 128] qkv buffer; "
+                       f"{CHAIN_STEPS} steps of the six calls")
+        extra_workloads["chain10s"] = res
+        checks.append(("chain10s", got3, idx3, c10, args.warmup + CHAIN_STEPS, False, True))
 
-    K = args.steps
-    n_ops = len(step)
-    # event pairs around every launch; without a flush consecutive launches share
-    # their boundary event
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_ops)] for _ in range(K)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record()
-    for s in range(K):
-        for i, (_, fn) in enumerate(step):
-            if flush is not None:
-                flush()
-            if flush is not None or i == 0:
-                ev[s][2 * i].record()
-            fn()
-            ev[s][2 * i + 1].record()
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    def launch_ms(s, i):
-        first = ev[s][2 * i] if (flush is not None or i == 0) else ev[s][2 * i - 1]
-        return first.elapsed_time(ev[s][2 * i + 1])
-
-    per_op_ms = {}
-    per_op_n = {}
-    per_op_all = {}
-    for s in range(K):
-        for i, (name, _) in enumerate(step):
-            ms = launch_ms(s, i)
-            per_op_ms[name] = per_op_ms.get(name, 0.0) + ms
-            per_op_n[name] = per_op_n.get(name, 0) + 1
-            per_op_all.setdefault(name, []).append(ms)
-    if flush is None:
-        ms_per_step = start.elapsed_time(stop) / K
-    else:  # the flushes between launches are not part of a step
-        ms_per_step = sum(launch_ms(s, i) for s in range(K) for i in range(n_ops)) / K
-    step_bytes = sum(op_bytes(name, N, c, x_bytes) for name, _ in step)
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    per_op = {}
-    for name in per_op_ms:
-        avg = per_op_ms[name] / per_op_n[name]
-        b = op_bytes(name, N, c, x_bytes)
-        ts = sorted(per_op_all[name])
-        per_op[name] = {"avg_ms": round(avg, 4), "median_ms": round(ts[len(ts) // 2], 4),
-                        "min_ms": round(ts[0], 4), "launches": len(ts),
-                        "bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1),
-                        "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                        "frac_of_copy_ceiling": round(b / (avg * 1e-3) / 1e9 / copy_gbps, 4)}
-
-    # Step-reuse test (residual difference between neighbouring steps): timed on its
-    # own, outside the block step, since a block runs it at most once per step.
-    extra_ops = {}
-    if not chain:
-        x_prev = torch.empty_like(t["x"])
-        h3gen.fill_device(x_prev, "x_prev")
-        l1_out = torch.zeros(3, dtype=torch.float64, device=dev)
-        ws = torch.empty(max(16, h3.h3f_residual_l1_workspace_bytes(N, c["D"], t["x"].dtype)),
-                         dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            h3.h3f_residual_l1(l1_out, t["x"], x_prev, ws)
-        torch.cuda.synchronize()
-        avg = time_calls(lambda: h3.h3f_residual_l1(l1_out, t["x"], x_prev, ws), K)
-        b = 2 * N * c["D"] * 2
-        extra_ops["residual_l1"] = {"avg_ms": round(avg, 4), "bytes": b,
-                                    "GBps": round(b / (avg * 1e-3) / 1e9, 1),
-                                    "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
-        del x_prev, ws
-
-        # Block-sparse attention router on the step's post-RoPE q / k (what attention
-        # reads), blocks of 128 tokens, sparsity 0.8, a routed step.
-        blk, sp = 128, 0.8
-        nb, keep, need = h3.h3f_subblock_plan(N, c["heads"], c["Dh"], blk, sp, 10)
-        kv = torch.empty(c["heads"], nb, keep, dtype=torch.int32, device=dev)
-        sc = torch.empty(c["heads"], nb, nb, dtype=torch.float32, device=dev)
-        ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            h3.h3f_subblock_route(kv, sc, t["q_out"], t["k_out"], blk, sp, 10, ws)
-        torch.cuda.synchronize()
-        avg = time_calls(lambda: h3.h3f_subblock_route(kv, sc, t["q_out"], t["k_out"], blk, sp,
-                                                       10, ws), K)
-        b = router_bytes(N, c, nb, keep)
-        extra_ops["subblock_route"] = {
-            "avg_ms": round(avg, 4), "bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1),
-            "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "block": blk, "sparsity": sp, "n_blocks": nb, "keep": keep,
-            "score_flops": 2 * c["heads"] * nb * nb * c["Dh"]}
-
-        # A routed step with the router's pooling fused into the QK operator: the
-        # QK call that also writes the block means, then the route from them.
-        def qk_pool():
-            h3.h3f_qk_rmsnorm_rope3d_pool(t["q_out"], t["k_out"], t["q"], t["k"], t["q_weight"],
-                                          t["k_weight"], rope, blk, ws)
-
-        def route_pooled():
-            h3.h3f_subblock_route_pooled(kv, sc, N, c["heads"], blk, sp, 10, ws)
-
-        for _ in range(3):
-            qk_pool()
-            route_pooled()
-        torch.cuda.synchronize()
-        a_qp = time_calls(qk_pool, K)
-        a_rp = time_calls(route_pooled, K)
-        b_qp = op_bytes("qk", N, c, x_bytes) + 2 * c["heads"] * nb * c["Dh"] * 4
-        b_rp = c["heads"] * nb * nb * 4 + c["heads"] * nb * keep * 4 + 2 * c["heads"] * nb * c["Dh"] * 4
-        extra_ops["qk_rmsnorm_rope3d_pool"] = {
-            "avg_ms": round(a_qp, 4), "bytes": b_qp, "GBps": round(b_qp / (a_qp * 1e-3) / 1e9, 1),
-            "frac_of_peak": round(b_qp / (a_qp * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
-        extra_ops["subblock_route_pooled"] = {
-            "avg_ms": round(a_rp, 4), "bytes": b_rp, "GBps": round(b_rp / (a_rp * 1e-3) / 1e9, 1)}
-        extra_ops["routed_qk_step_ms"] = {
-            "separate": round(per_op["qk"]["avg_ms"] + avg, 4), "fused": round(a_qp + a_rp, 4)}
-        del kv, sc, ws
-
-    dom = "swiglu"
+    dom = "swiglu"  # the largest single kernel of the step (10.4 GB per launch at 5 s)
     roofline = {"bound": "hbm", "achieved": per_op[dom]["GBps"], "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": per_op[dom]["frac_of_peak"],
                 "traffic": traffic_from_profiles(dom, args.workload),
                 "kernel": "swiglu_kernel<bf16,8>", "bytes_per_launch": per_op[dom]["bytes"],
                 "avg_launch_ms": per_op[dom]["avg_ms"]}
 
+    # ---- oracle leg (after every timed region): CPU baseline and output check ----
+    from bench_check import check_block_step
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(c, min(args.cpu_rows, N), x_bytes, seed=args.seed)
+    check = {}
+    worst = 0.0
+    for label, g_rows, g_idx, grid, n_steps, fz, ch in checks:
+        r = check_block_step(g_rows, g_idx, grid, n_steps, args.seed, fused=fz, chain=ch)
+        check[label] = r
+        worst = max([worst] + list(r["per_op"].values()))
+        table = per_op if label == "headline" else extra_workloads[label]["per_op"]
+        for op, e in r["per_op"].items():
+            table[op]["max_err_over_tol"] = e
+    check["max_err_over_tol"] = round(worst, 4)
+    check["ok"] = worst <= 1.0
 
     wl = {"5s": "5 s 1344x768 clip token shape", "10s": "10 s 1344x768 clip token shape",
           "chain10s": "10 s shape, fp32 residual stream, packed qkv, block epilogue chain"}
@@ -447,12 +555,12 @@ def main():
     }
     out = {
         "metric": "achieved HBM GB/s (and % of peak) per fused op at 5 s 1344x768 token shape",
-        "value": round(value, 1),
+        "value": head["value_GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -460,17 +568,24 @@ def main():
         "storage_dtype": ("fp32 residual stream, bf16 activations" if chain else "bf16"),
         "data": "synthetic (seeded counter-based generator, N(0,1)-like activations)",
         "config": config,
-        "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
+        "frac_of_peak": round(head["value_GBps"] / PEAK_HBM_GBPS, 4),
         "per_op": per_op,
+        "check": check,
+        "references": refs,
+        "copy_ceiling_GBps": refs["stream_copy_GBps"],
         "extra_ops": extra_ops,
-        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "extra_workloads": extra_workloads,
         "cache_flush_mb": flush_mb,
         "seed": args.seed,
-        "wall_s_timed_region": round(wall, 4),
+        "wall_s_timed_region": head["wall_s_timed_region"],
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    if not check["ok"]:
+        print(f"bench.py: timed outputs differ from the oracle beyond tolerance "
+              f"(max err/tol {worst:.3f})", file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":
