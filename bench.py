@@ -529,6 +529,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(c, min(args.cpu_rows, N), x_bytes, seed=args.seed)
+        if "chain10s" in extra_workloads:
+            # the oracle on the chain's own form (fp32 residual stream, 10 s grid)
+            extra_workloads["chain10s"]["cpu_baseline"] = _time_oracle(
+                GRIDS["10s"], 8192, 4, 5.0, args.seed)
     check = {}
     worst = 0.0
     for label, g_rows, g_idx, grid, n_steps, fz, ch in checks:
