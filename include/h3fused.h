@@ -45,7 +45,9 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *     stream).  A fault inside a kernel surfaces at the caller's next
  *     synchronisation.  Launch failures return H3F_ERR_LAUNCH.
- *   - Every entry point is reentrant and keeps no state between calls.
+ *   - Every entry point is reentrant and keeps no state between calls, except
+ *     h3f_residual_l1_noalloc, whose partial sums live in a device array the
+ *     library owns (see there: calls that overlap on one GPU race).
  */
 #ifndef H3FUSED_H
 #define H3FUSED_H
