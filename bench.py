@@ -66,8 +66,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="5s", choices=sorted(GRIDS) + ["chain10s"])
-    ap.add_argument("--fused", action="store_true",
-                    help="fuse each gated residual with the AdaLN that follows it")
+    ap.add_argument("--form", default="separate", choices=FORMS,
+                    help="the headline block's form: the six separate operators, or each "
+                         "gated residual fused into the next AdaLN (four calls)")
+    ap.add_argument("--fused", action="store_true", help="same as --form fused")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the bandwidth references and the headline step (no "
                          "extra ops, other block form or chain)")
@@ -171,9 +173,14 @@ def build_inputs(c, N, torch, h3gen, dev, chain=False, seed=0):
     return t
 
 
-def make_step(h3, t, rope, fused):
-    """The fused calls of one DiT block, each tagged with its operator name."""
-    if not fused:
+FORMS = ("separate", "fused")
+
+
+def make_step(h3, t, rope, form):
+    """The fused calls of one DiT block, each tagged with its operator name.
+    separate: the six operators; fused: each gated residual fused into the AdaLN
+    that follows it (four calls)."""
+    if form == "separate":
         return [
             ("adaln", lambda: h3.h3f_adaln_modulate(t["y"], t["x"], t["shift"], t["scale"])),
             ("qk", lambda: h3.h3f_qk_rmsnorm_rope3d(t["q_out"], t["k_out"], t["q"], t["k"],
@@ -287,7 +294,7 @@ def measure_references(torch, h3, dev):
     return ref
 
 
-def block_workload(args, torch, h3, h3gen, dev, c, chain, fused, K, W, best_copy, flush=None):
+def block_workload(args, torch, h3, h3gen, dev, c, chain, form, K, W, best_copy, flush=None):
     """Time K block steps (after W warmup steps) at grid c and fetch the sampled
     output rows for the oracle check.  Returns (result dict, fetched rows, idx)."""
     from bench_check import fetch_rows, sample_rows
@@ -296,7 +303,7 @@ def block_workload(args, torch, h3, h3gen, dev, c, chain, fused, K, W, best_copy
     x_bytes = 4 if chain else 2
     t = build_inputs(c, N, torch, h3gen, dev, chain=chain, seed=args.seed)
     rope = h3.make_rope(c["T"], c["H"], c["W"], c["A"], c["split"])
-    step = make_step(h3, t, rope, fused)
+    step = make_step(h3, t, rope, form)
     ms_per_step, per_op_all, wall = time_step(torch, step, K, W, flush)
     step_bytes = sum(op_bytes(name, N, c, x_bytes) for name, _ in step)
     idx = sample_rows(N, N - c["A"])
@@ -483,38 +490,41 @@ def main():
     checks = []  # (label, rows, idx, grid, steps run, fused, chain)
 
     # ---- the headline step ----
-    head, got, idx, t, rope = block_workload(args, torch, h3, h3gen, dev, c, chain, args.fused,
+    form = "fused" if args.fused else args.form
+    head, got, idx, t, rope = block_workload(args, torch, h3, h3gen, dev, c, chain, form,
                                              args.steps, args.warmup, best_copy, flush)
-    checks.append(("headline", got, idx, c, args.warmup + args.steps, args.fused, chain))
+    checks.append(("headline", got, idx, c, args.warmup + args.steps, form, chain))
     per_op = head["per_op"]
 
     extra_ops, extra_workloads = {}, {}
-    if extras and args.workload == "5s" and not args.fused:
+    if extras and args.workload == "5s" and "qk" in per_op:
         extra_ops = extra_ops_5s(args, torch, h3, h3gen, dev, c, t, rope, args.steps, per_op)
     del t
     torch.cuda.empty_cache()
     if extras and args.workload == "5s":
-        # the other form of the same block: gated residual fused into the next AdaLN
-        # (or, when the headline is the fused block, the six separate calls)
-        other = not args.fused
-        res, got2, idx2, t, _ = block_workload(args, torch, h3, h3gen, dev, c, False, other,
+        # the other forms of the same block
+        for other in FORMS:
+            if other == form:
+                continue
+            res, g2, i2, t, _ = block_workload(args, torch, h3, h3gen, dev, c, False, other,
                                                args.steps, args.warmup, best_copy)
-        del t
-        torch.cuda.empty_cache()
-        extra_workloads["fused_block_5s" if other else "separate_block_5s"] = res
-        checks.append(("fused_block_5s" if other else "separate_block_5s", got2, idx2, c,
-                       args.warmup + args.steps, other, False))
+            del t
+            torch.cuda.empty_cache()
+            label = f"{other}_block_5s"
+            extra_workloads[label] = res
+            checks.append((label, g2, i2, c, args.warmup + args.steps, other, False))
         # the 10 s fp32-residual packed-qkv epilogue chain (6 calls per step)
         c10 = GRIDS["10s"]
-        res, got3, idx3, t, _ = block_workload(args, torch, h3, h3gen, dev, c10, True, False,
-                                               CHAIN_STEPS, args.warmup, best_copy)
+        res, got3, idx3, t, _ = block_workload(args, torch, h3, h3gen, dev, c10, True,
+                                               "separate", CHAIN_STEPS, args.warmup, best_copy)
         del t
         torch.cuda.empty_cache()
         res["note"] = ("10 s shape, fp32 residual stream and modulation, bf16 activations, "
                        "q/k read strided from a packed [tokens, 3, 40, 128] qkv buffer; "
                        f"{CHAIN_STEPS} steps of the six calls")
         extra_workloads["chain10s"] = res
-        checks.append(("chain10s", got3, idx3, c10, args.warmup + CHAIN_STEPS, False, True))
+        checks.append(("chain10s", got3, idx3, c10, args.warmup + CHAIN_STEPS, "separate",
+                       True))
 
     dom = "swiglu"  # the largest single kernel of the step (10.4 GB per launch at 5 s)
     roofline = {"bound": "hbm", "achieved": per_op[dom]["GBps"], "peak": PEAK_HBM_GBPS,
@@ -535,8 +545,9 @@ def main():
                 GRIDS["10s"], 8192, 4, 5.0, args.seed)
     check = {}
     worst = 0.0
-    for label, g_rows, g_idx, grid, n_steps, fz, ch in checks:
-        r = check_block_step(g_rows, g_idx, grid, n_steps, args.seed, fused=fz, chain=ch)
+    for label, g_rows, g_idx, grid, n_steps, fm, ch in checks:
+        r = check_block_step(g_rows, g_idx, grid, n_steps, args.seed, fused=fm == "fused",
+                             chain=ch)
         check[label] = r
         worst = max([worst] + list(r["per_op"].values()))
         table = per_op if label == "headline" else extra_workloads[label]["per_op"]
@@ -551,11 +562,12 @@ def main():
         "workload": (wl.get(args.workload, f"roofline sweep, hidden {c['D']}") +
                      f": {N} tokens ({c['T']}x{c['H']}x{c['W']} video + {c['A']} audio), "
                      f"hidden {c['D']}, {c['heads']}x{c['Dh']} heads, RoPE split "
-                     f"{'/'.join(map(str, c['split']))}, SwiGLU inner {c['F']}; one DiT block's "
-                     f"{'four fused (gated+AdaLN fused)' if args.fused else 'six'} fused-op calls "
-                     f"per step"),
+                     f"{'/'.join(map(str, c['split']))}, SwiGLU inner {c['F']}; one DiT block: "
+                     + {"separate": "six fused-op calls per step",
+                        "fused": "four fused-op calls per step (gated residual fused into "
+                                 "AdaLN)"}[form]),
         "tokens": N, "hidden": c["D"], "heads": c["heads"], "head_dim": c["Dh"],
-        "swiglu_inner": c["F"], "fused_gated_adaln": bool(args.fused),
+        "swiglu_inner": c["F"], "block_form": form,
     }
     out = {
         "metric": "achieved HBM GB/s (and % of peak) per fused op at 5 s 1344x768 token shape",

@@ -87,7 +87,6 @@ def _declare(L):
     L.oracle_gated_residual_adaln.argtypes = [_p, _int, _p, _int, _p, _p, _int,
                                               _p, _p, _p, _i64, _i64, _i64, _f]
     L.oracle_residual_l1.argtypes = [_p, _p, _p, _int, _i64, _i64]
-    L.oracle_ln_segment_stats.argtypes = [_p, _p, _int, _i64, _i64, _i64]
     L.oracle_subblock_pool.argtypes = [_p, _p, _int, _i64, _i32, _i32, _i32]
     L.oracle_subblock_scores.argtypes = [_p, _p, _p, _i32, _i64, _i64, _i32]
     L.oracle_subblock_keep.argtypes = [_i64, _d, _i32, _i32]
@@ -265,17 +264,6 @@ def gated_residual_adaln(x, h, gate, shift, scale, eps=1e-6, y_dtype=None,
                                       _ptr(scale), _ptr(g), max(rpg, 1), rows,
                                       D, eps)
     return x, y
-
-
-def ln_segment_stats(x, seg=256):
-    """[rows, hidden / seg, 2] float64: (mean, sum of squared deviations) of each
-    seg-element segment of each row (hidden must be a multiple of seg)."""
-    x = np.ascontiguousarray(x)
-    rows, hidden = x.shape
-    assert hidden % seg == 0
-    out = np.zeros((rows, hidden // seg, 2), dtype=np.float64)
-    lib().oracle_ln_segment_stats(_ptr(out), _ptr(x), _dt(x), rows, hidden, seg)
-    return out
 
 
 def residual_l1(cur, prev):

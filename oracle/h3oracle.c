@@ -145,37 +145,6 @@ void oracle_adaln_modulate(void* y, int y_dtype, const void* x, int x_dtype,
 }
 
 /* ---------------------------------------------------------------------------
- * LayerNorm statistics of row segments.  The mean and variance a LayerNorm
- * row needs (Ba et al. 2016, eq. 3-4) can be assembled from the statistics of
- * equal-size segments of the row: with segment means m_t and sums of squared
- * deviations M2_t over n elements each, the row mean is the average of the
- * m_t and the row's sum of squared deviations is
- * sum_t M2_t + n * sum_t (m_t - mean)^2 (Chan, Golub & LeVeque 1979, the
- * pairwise combination applied to equal-size groups).  This lets the kernel
- * that writes x hand AdaLN its statistics.  Definition: out[r, t] = (m_t,
- * M2_t) of elements [t * seg, (t + 1) * seg) of row r, in double.
- * ------------------------------------------------------------------------- */
-void oracle_ln_segment_stats(double* out, const void* x, int x_dtype, int64_t rows,
-                             int64_t hidden, int64_t seg) {
-    const int64_t nseg = hidden / seg;
-#pragma omp parallel for schedule(static)
-    for (int64_t r = 0; r < rows; ++r) {
-        for (int64_t t = 0; t < nseg; ++t) {
-            double sum = 0.0;
-            for (int64_t c = 0; c < seg; ++c) sum += ld(x, x_dtype, r * hidden + t * seg + c);
-            const double m = sum / (double)seg;
-            double m2 = 0.0;
-            for (int64_t c = 0; c < seg; ++c) {
-                const double d = ld(x, x_dtype, r * hidden + t * seg + c) - m;
-                m2 += d * d;
-            }
-            out[2 * (r * nseg + t)] = m;
-            out[2 * (r * nseg + t) + 1] = m2;
-        }
-    }
-}
-
-/* ---------------------------------------------------------------------------
  * LayerNorm with its own affine gain and bias (Ba, Kiros & Hinton 2016, eq. 4:
  * g * (a - mean) / sigma + b), then the AdaLN modulation of that output.  A
  * variant of the reading above for models whose LayerNorm keeps its affine

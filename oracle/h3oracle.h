@@ -87,13 +87,6 @@ void oracle_adaln_modulate(void* y, int y_dtype, const void* x, int x_dtype,
  * y[r,:] = (gamma * (x[r,:] - mean) / sqrt(var + eps) + beta) * (1 + scale[g,:])
  *          + shift[g,:]
  * gamma, beta: [hidden] of mod_dtype, shared by all rows; the rest as above. */
-/* Segment statistics of LayerNorm rows: out[r, t] = (mean, sum of squared
- * deviations) of elements [t*seg, (t+1)*seg) of row r (hidden a multiple of
- * seg), in double; the row's mean and variance follow by the equal-size
- * parallel combination (Chan, Golub & LeVeque 1979). */
-void oracle_ln_segment_stats(double* out, const void* x, int x_dtype, int64_t rows,
-                             int64_t hidden, int64_t seg);
-
 void oracle_adaln_affine_modulate(void* y, int y_dtype, const void* x, int x_dtype,
                                   const void* gamma, const void* beta,
                                   const void* shift, const void* scale, int mod_dtype,

@@ -41,10 +41,6 @@ MUTANTS = {
     "affine_after_modulation": ("st(y, y_dtype, r * D + c, ln * (1.0 + sc) + sh);",
                                 "st(y, y_dtype, r * D + c, (ln - ld(beta, mod_dtype, c)) * (1.0 + sc) + sh + ld(beta, mod_dtype, c));"),
     "affine_gamma_beta_swapped": ("const double ln = ld(gamma, mod_dtype, c) *", "const double ln = ld(beta, mod_dtype, c) *"),
-    "lnstats_raw_square_sum": ("const double d = ld(x, x_dtype, r * hidden + t * seg + c) - m;",
-                               "const double d = ld(x, x_dtype, r * hidden + t * seg + c);"),
-    "lnstats_wrong_segment": ("sum += ld(x, x_dtype, r * hidden + t * seg + c);",
-                              "sum += ld(x, x_dtype, r * hidden + c);"),
     "subblock_sum_not_mean": ("= s / (double)(r1 - r0);", "= s;"),
     "subblock_full_block_divisor": ("= s / (double)(r1 - r0);", "= s / (double)block;"),
     "subblock_wrong_head": ("ld(x, dtype, (r * heads + h) * head_dim + d)",

@@ -520,40 +520,6 @@ def test_residual_l1():
 
 
 # ----------------------------------------------------------------------------------
-# LayerNorm segment statistics (what the residual kernel hands AdaLN)
-# ----------------------------------------------------------------------------------
-
-def test_ln_segment_stats_hand_values():
-    # row 1..8 in two segments of 4: means 2.5 and 6.5, squared deviations
-    # 1.5^2 + 0.5^2 + 0.5^2 + 1.5^2 = 5 each
-    st = oracle.ln_segment_stats(f32([np.arange(1, 9)]), seg=4)
-    assert st.shape == (1, 2, 2)
-    assert st[0].tolist() == [[2.5, 5.0], [6.5, 5.0]]
-    # a constant segment: its value and exactly zero spread
-    st = oracle.ln_segment_stats(f32([[3.25] * 8 + [-1.0] * 8]), seg=8)
-    assert st[0].tolist() == [[3.25, 0.0], [-1.0, 0.0]]
-
-
-@pytest.mark.parametrize("seg,D,kind", [(256, 5120, "bf16"), (64, 1024, "f32"), (256, 256, "f32")])
-def test_ln_segment_stats_combine_to_row_moments(seg, D, kind):
-    # the equal-size parallel combination of the segment statistics gives the row's
-    # mean and (biased) variance as numpy computes them directly
-    x = RNG.standard_normal((7, D)) * 3 + RNG.standard_normal((7, 1)) * 5
-    x = bf16_bits(x) if kind == "bf16" else f32(x)
-    st = oracle.ln_segment_stats(x, seg=seg)
-    m, m2 = st[..., 0], st[..., 1]
-    mean = m.mean(axis=1)
-    var = (m2.sum(axis=1) + seg * ((m - mean[:, None]) ** 2).sum(axis=1)) / D
-    xd = as_f64(x)
-    np.testing.assert_allclose(mean, xd.mean(axis=1), rtol=1e-12, atol=1e-13)
-    np.testing.assert_allclose(var, xd.var(axis=1), rtol=1e-12)
-    # and each segment on its own
-    seg0 = xd[:, :seg]
-    np.testing.assert_allclose(m[:, 0], seg0.mean(axis=1), rtol=1e-12, atol=1e-13)
-    np.testing.assert_allclose(m2[:, 0], seg0.var(axis=1) * seg, rtol=1e-12)
-
-
-# ----------------------------------------------------------------------------------
 # block-sparse attention router (SubBlock)
 # ----------------------------------------------------------------------------------
 
