@@ -259,7 +259,8 @@ h3f_status_t h3f_residual_l1(double* out, const void* cur, int64_t cur_row_strid
  *   is rejected with H3F_ERR_WORKSPACE (bf16 at hidden 5120: up to 838,860
  *   rows).  Each GPU the library runs on holds its own copy of the array until
  *   the process ends; its address is looked up once per device, on the first
- *   call with that device current (H3F_ERR_LAUNCH if the lookup fails).
+ *   call with that device current (H3F_ERR_LAUNCH if the lookup fails) -- a
+ *   caller that captures the call in a graph makes one call before capturing.
  *   Sharing: every call on one GPU uses that GPU's array, which keeps the last
  *   call's partial sums (each call writes all the sums it reads, so no clearing
  *   is needed).  Calls that may run concurrently on one GPU (other streams,

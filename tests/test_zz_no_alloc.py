@@ -94,3 +94,36 @@ def test_noalloc_through_c_abi_and_limit():
                                   host("x_prev", 64, 5120, "bf16", seed=4))
     g = out.cpu().numpy()
     assert abs(g[0] - num) <= L1_RTOL * num and abs(g[1] - den) <= L1_RTOL * den
+
+
+def test_noalloc_captured_in_a_graph():
+    # the callers this entry point is for: a captured graph replayed with eager work
+    # (including another no-allocation call, on the same scratch, ordered on the
+    # stream) between the replays; every replay equals the eager result bit for bit
+    cur, prev = _pair(30001, 5120, "bf16", 0, 5)
+    other_c, other_p = _pair(777, 3072, "bf16", 0, 6)
+    want = torch.zeros(3, dtype=torch.float64, device=DEV)
+    h3.h3f_residual_l1_noalloc(want, cur, prev)  # eager first: the device address is looked up
+    out = torch.zeros(3, dtype=torch.float64, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        h3.h3f_residual_l1_noalloc(out, cur, prev)
+    torch.cuda.synchronize()
+    side = torch.zeros(3, dtype=torch.float64, device=DEV)
+    side_ref = torch.zeros(3, dtype=torch.float64, device=DEV)
+    h3.h3f_residual_l1(side_ref, other_c, other_p)
+    for rep in range(4):
+        out.fill_(-1.0)
+        g.replay()
+        h3.h3f_residual_l1_noalloc(side, other_c, other_p)  # same scratch, after the replay
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {rep}"
+        assert torch.equal(side, side_ref), f"eager call after replay {rep}"
+    # the graph holds pointers: new contents are followed
+    prev.mul_(0.5)
+    want2 = torch.zeros(3, dtype=torch.float64, device=DEV)
+    h3.h3f_residual_l1(want2, cur, prev)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, want2) and not torch.equal(want2, want)
