@@ -20,7 +20,8 @@ headline's timed region:
     hipMemcpyDtoD (torch copy_), a read-only and a write-only stream;
   * the same block with each gated residual fused into the AdaLN that follows
     it (four calls per step);
-  * the step-reuse residual difference and the block-sparse attention router;
+  * the step-reuse residual difference and the block-sparse attention router
+    (also at --workload 10s and the sweep shapes);
   * the 10 s fp32-residual packed-qkv block epilogue chain, 50 steps.
 After all timing, the oracle leg runs on the host: the CPU baseline (the oracle
 timed on a bounded sample of the workload) and the check of every timed step's
@@ -318,7 +319,7 @@ def block_workload(args, torch, h3, h3gen, dev, c, chain, form, K, W, best_copy,
     return res, got, idx, t, rope
 
 
-def extra_ops_5s(args, torch, h3, h3gen, dev, c, t, rope, K, per_op):
+def time_extra_ops(args, torch, h3, h3gen, dev, c, t, rope, K, per_op):
     """Step-reuse residual difference and the block-sparse attention router,
     each timed on its own (a block runs them at most once per step)."""
     N = n_tokens(c)
@@ -349,11 +350,11 @@ def extra_ops_5s(args, torch, h3, h3gen, dev, c, t, rope, K, per_op):
     del x_prev, ws
 
     # router on the step's post-RoPE q / k (what attention reads), blocks of 128
-    # tokens, sparsity 0.8, a routed step
+    # tokens, sparsity 0.8, a routed step; score rows padded to 128 bytes
     blk, sp = 128, 0.8
     nb, keep, need = h3.h3f_subblock_plan(N, c["heads"], c["Dh"], blk, sp, 10)
     kv = torch.empty(c["heads"], nb, keep, dtype=torch.int32, device=dev)
-    sc = torch.empty(c["heads"], nb, nb, dtype=torch.float32, device=dev)
+    sc = h3.scores_view(c["heads"], nb, dev)
     ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
     for _ in range(3):
         h3.h3f_subblock_route(kv, sc, t["q_out"], t["k_out"], blk, sp, 10, ws)
@@ -365,7 +366,7 @@ def extra_ops_5s(args, torch, h3, h3gen, dev, c, t, rope, K, per_op):
         "avg_ms": round(avg, 4), "bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1),
         "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "block": blk, "sparsity": sp, "n_blocks": nb, "keep": keep,
-        "score_flops": 2 * c["heads"] * nb * nb * c["Dh"]}
+        "scores_row_stride": sc.stride(1), "score_flops": 2 * c["heads"] * nb * nb * c["Dh"]}
 
     # a routed step with the router's pooling fused into the QK operator: the QK
     # call that also writes the block means, then the route from them
@@ -497,8 +498,8 @@ def main():
     per_op = head["per_op"]
 
     extra_ops, extra_workloads = {}, {}
-    if extras and args.workload == "5s" and "qk" in per_op:
-        extra_ops = extra_ops_5s(args, torch, h3, h3gen, dev, c, t, rope, args.steps, per_op)
+    if extras and not chain and "qk" in per_op:
+        extra_ops = time_extra_ops(args, torch, h3, h3gen, dev, c, t, rope, args.steps, per_op)
     del t
     torch.cuda.empty_cache()
     if extras and args.workload == "5s":

@@ -304,17 +304,25 @@ h3f_status_t h3f_residual_l1_noalloc(double* out, const void* cur, int64_t cur_r
  * row / head strides in elements (e.g. the q, k outputs of
  * h3f_qk_rmsnorm_rope3d; strides multiples of 8, pointers 16-byte aligned).
  * kv_blocks: device int32 [heads, n_blocks, keep], dense, 4-byte aligned.
- * scores: device fp32 [heads, n_blocks, n_blocks], dense, 16-byte aligned,
- * written on routed steps only (but required on every step).  workspace:
- * device scratch of at least workspace_bytes (16-byte aligned, no
- * initialisation needed; calls sharing one must be ordered on one stream).  Outputs and workspace must not overlap
- * each other or q, k.  On a dense step (step < H3F_SUBBLOCK_FIRST_STEP) the
- * call only writes kv_blocks[h,i,:] = 0..n_blocks-1 and reads neither q nor k.
+ * scores: device fp32 [heads, n_blocks, n_blocks], 16-byte aligned, row
+ * (h, i) starting (h * n_blocks + i) * scores_row_stride floats in;
+ * scores_row_stride >= n_blocks (n_blocks for dense rows).  Only the first
+ * n_blocks floats of a row are written, on routed steps only (the pointer is
+ * required on every step).  A stride that is a multiple of 32 (128-byte rows)
+ * lets every cache line of scores be written whole by one wavefront, which
+ * dense rows of most block counts do not allow.  workspace: device scratch of
+ * at least workspace_bytes (16-byte aligned, no initialisation needed; calls
+ * sharing one must be ordered on one stream).  Outputs and workspace must not
+ * overlap each other or q, k.  On a dense step (step <
+ * H3F_SUBBLOCK_FIRST_STEP) the call only writes kv_blocks[h,i,:] =
+ * 0..n_blocks-1 and reads neither q nor k.
  * Errors: H3F_ERR_UNSUPPORTED for a dtype other than bf16, head_dim != 128,
  * rows < 4096 (unlike the per-token operators, rows == 0 is not a no-op),
- * n_blocks > 8192, heads > 4096 or a stride above 2^31 elements;
+ * n_blocks > 8192, heads > 4096, a q / k stride above 2^31 elements or one
+ * head's scores above 2^32 - 16 bytes (n_blocks * scores_row_stride * 4);
  * H3F_ERR_BAD_VALUE for sparsity outside [0, 1) or step < 1;
- * H3F_ERR_BAD_SHAPE for block < 1 or heads < 1.
+ * H3F_ERR_BAD_SHAPE for block < 1 or heads < 1; H3F_ERR_BAD_STRIDE for
+ * scores_row_stride < n_blocks.
  * Deterministic: fixed summation order; bit-identical run to run.  -0 and +0
  * scores rank equal; with non-finite q / k values the kept lists are still
  * exactly keep valid, ascending block indices, but which ones is unspecified.
@@ -323,7 +331,7 @@ h3f_status_t h3f_residual_l1_noalloc(double* out, const void* cur, int64_t cur_r
 h3f_status_t h3f_subblock_plan(int64_t rows, int32_t heads, int32_t head_dim, int32_t block,
                                double sparsity, int32_t step, int32_t* n_blocks, int32_t* keep,
                                size_t* workspace_bytes);
-h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores,
+h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, int64_t scores_row_stride,
                                 const void* q, int64_t q_row_stride, int64_t q_head_stride,
                                 const void* k, int64_t k_row_stride, int64_t k_head_stride,
                                 h3f_dtype_t dtype, int64_t rows, int32_t heads,
@@ -372,9 +380,10 @@ h3f_status_t h3f_qk_rmsnorm_rope3d_pool(void* q_out, int64_t q_out_row_stride,
  * and determinism as h3f_subblock_route; on a dense step the workspace is
  * neither needed nor read.
  */
-h3f_status_t h3f_subblock_route_pooled(int32_t* kv_blocks, float* scores, int64_t rows,
-                                       int32_t heads, int32_t head_dim, int32_t block,
-                                       double sparsity, int32_t step, const void* workspace,
+h3f_status_t h3f_subblock_route_pooled(int32_t* kv_blocks, float* scores,
+                                       int64_t scores_row_stride, int64_t rows, int32_t heads,
+                                       int32_t head_dim, int32_t block, double sparsity,
+                                       int32_t step, const void* workspace,
                                        size_t workspace_bytes, void* stream);
 
 /*

@@ -86,15 +86,15 @@ int main() {
     EXPECT(h3f_subblock_plan(125120, 40, 128, 128, 0.8, 10, &nb, &keep, &ws), H3F_OK);
     EXPECT(nb, 978);
     EXPECT(keep, 196);
-    EXPECT(h3f_subblock_route(static_cast<int32_t*>(A(0)), static_cast<float*>(A(1)), A(2),
+    EXPECT(h3f_subblock_route(static_cast<int32_t*>(A(0)), static_cast<float*>(A(1)), 32, A(2),
                               huge & ~int64_t(7), 128, A(3), 1024, 128, B, 4096, 8, 128, 128,
                               0.8, 10, A(4), 1 << 20, nullptr), H3F_ERR_UNSUPPORTED);
-    EXPECT(h3f_subblock_route(static_cast<int32_t*>(A(0)), static_cast<float*>(A(1)), A(2), 1024,
-                              big, A(3), 1024, 128, B, 4096, 8, 128, 128, 0.8, 10, A(4), 1 << 20,
-                              nullptr), H3F_ERR_UNSUPPORTED);
-    EXPECT(h3f_subblock_route(static_cast<int32_t*>(A(0)), static_cast<float*>(A(1)), A(2), 1024,
-                              128, A(3), 1024, 128, B, int64_t(1) << 44, 8, 128, INT32_MAX, 0.8,
-                              10, A(4), 1 << 20, nullptr), H3F_ERR_UNSUPPORTED);
+    EXPECT(h3f_subblock_route(static_cast<int32_t*>(A(0)), static_cast<float*>(A(1)), 32, A(2),
+                              1024, big, A(3), 1024, 128, B, 4096, 8, 128, 128, 0.8, 10, A(4),
+                              1 << 20, nullptr), H3F_ERR_UNSUPPORTED);
+    EXPECT(h3f_subblock_route(static_cast<int32_t*>(A(0)), static_cast<float*>(A(1)), 32, A(2),
+                              1024, 128, A(3), 1024, 128, B, int64_t(1) << 44, 8, 128,
+                              INT32_MAX, 0.8, 10, A(4), 1 << 20, nullptr), H3F_ERR_UNSUPPORTED);
     // QK with the router pooling fused in, and the route from pooled means
     EXPECT(h3f_qk_rmsnorm_rope3d_pool(A(0), 5120, 128, A(1), 5120, 128, A(2), big, 128, A(3), 5120,
                                       128, A(4), A(5), B, 4096, 40, 128, 1e-6f, &r, 128, A(6),
@@ -102,12 +102,15 @@ int main() {
     EXPECT(h3f_qk_rmsnorm_rope3d_pool(A(0), 5120, 128, A(1), 5120, 128, A(2), 5120, 128, A(3),
                                       5120, 128, A(4), A(5), B, INT64_MAX, 40, 128, 1e-6f, &r, 128,
                                       A(6), 1 << 24, nullptr), H3F_ERR_UNSUPPORTED);
+    EXPECT(h3f_subblock_route(static_cast<int32_t*>(A(0)), static_cast<float*>(A(1)), INT64_MAX,
+                              A(2), 1024, 128, A(3), 1024, 128, B, 4096, 8, 128, 128, 0.8, 10,
+                              A(4), 1 << 20, nullptr), H3F_ERR_UNSUPPORTED);
     EXPECT(h3f_subblock_route_pooled(static_cast<int32_t*>(A(0)), static_cast<float*>(A(1)),
-                                     INT64_MAX, 8, 128, 1, 0.8, 10, A(2), 1 << 20, nullptr),
+                                     32, INT64_MAX, 8, 128, 1, 0.8, 10, A(2), 1 << 20, nullptr),
            H3F_ERR_UNSUPPORTED);
     EXPECT(h3f_subblock_route_pooled(static_cast<int32_t*>(A(0)), static_cast<float*>(A(1)),
-                                     int64_t(1) << 44, 8, 128, INT32_MAX, 0.8, 10, A(2), 1 << 20,
-                                     nullptr), H3F_ERR_UNSUPPORTED);
+                                     32, int64_t(1) << 44, 8, 128, INT32_MAX, 0.8, 10, A(2),
+                                     1 << 20, nullptr), H3F_ERR_UNSUPPORTED);
     // copy helper
     EXPECT(h3f_stream_copy(A(0), A(1), -16, nullptr), H3F_ERR_BAD_SHAPE);
     EXPECT(h3f_stream_copy(A(0), A(0), 1 << 20, nullptr), H3F_ERR_ALIASING);

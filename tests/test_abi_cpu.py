@@ -306,10 +306,11 @@ def test_subblock_plan_validation():
 def test_subblock_route_validation():
     # 4096 tokens x 8 heads x 128 (8 KB rows / 32 MB per tensor), 32 blocks of 128;
     # fake device addresses 256 MB apart: every call below fails validation.
-    def route(kv=A(0), sc=A(1), q=A(2), qrs=1024, qhs=128, k=A(3), krs=1024, khs=128, dt=BF16,
-              rows=4096, heads=8, hd=128, block=128, sp=0.8, step=10, ws=A(4), wsb=1 << 20):
-        return L.h3f_subblock_route(kv, sc, q, qrs, qhs, k, krs, khs, dt, rows, heads, hd, block,
-                                    sp, step, ws, wsb, None)
+    def route(kv=A(0), sc=A(1), ss=32, q=A(2), qrs=1024, qhs=128, k=A(3), krs=1024, khs=128,
+              dt=BF16, rows=4096, heads=8, hd=128, block=128, sp=0.8, step=10, ws=A(4),
+              wsb=1 << 20):
+        return L.h3f_subblock_route(kv, sc, ss, q, qrs, qhs, k, krs, khs, dt, rows, heads, hd,
+                                    block, sp, step, ws, wsb, None)
 
     assert route(kv=None) == NULLP
     assert route(sc=None) == NULLP
@@ -332,6 +333,16 @@ def test_subblock_route_validation():
     assert route(sc=A(2)) == ALIAS             # scores on top of q
     assert route(ws=P(0x10000000 + 64)) == ALIAS   # workspace inside kv_blocks
     assert route(kv=P(0x40000000 + 1024)) == ALIAS  # kv_blocks inside k
+    # scores rows: at least n_blocks (32) floats apart, one head's matrix within
+    # 32-bit offsets (2^32 - 16 bytes), padded rows part of the footprint
+    assert route(ss=31) == STRIDE
+    assert route(ss=0) == STRIDE
+    assert route(ss=-32) == STRIDE
+    assert route(ss=31, step=3) == STRIDE              # checked on dense steps too
+    assert route(ss=(1 << 32) // 128) == UNSUP          # 32 x 2^25 floats = 2^32 bytes
+    assert route(ss=1 << 62) == UNSUP                   # no overflow on the way
+    # 256 rows 256 B apart: only the last row's 128 written bytes reach q (A(2))
+    assert route(ss=64, sc=P(0x30000000 - 255 * 256 - 112)) == ALIAS
 
 
 def test_qk_pool_validation():
@@ -361,9 +372,10 @@ def test_qk_pool_validation():
 
 
 def test_route_pooled_validation():
-    def rp(kv=A(0), sc=A(1), rows=4096, heads=8, hd=128, block=128, sp=0.8, step=10, ws=A(2),
-           wsb=1 << 18):
-        return L.h3f_subblock_route_pooled(kv, sc, rows, heads, hd, block, sp, step, ws, wsb, None)
+    def rp(kv=A(0), sc=A(1), ss=32, rows=4096, heads=8, hd=128, block=128, sp=0.8, step=10,
+           ws=A(2), wsb=1 << 18):
+        return L.h3f_subblock_route_pooled(kv, sc, ss, rows, heads, hd, block, sp, step, ws, wsb,
+                                           None)
 
     assert rp(kv=None) == NULLP
     assert rp(sc=None) == NULLP
@@ -374,6 +386,9 @@ def test_route_pooled_validation():
     assert rp(ws=None) == WORKSPACE
     assert rp(wsb=(1 << 18) - 1) == WORKSPACE
     assert rp(ws=P(0x20000000 + 256)) == ALIAS     # workspace inside the scores
+    assert rp(ss=16) == STRIDE
+    assert rp(ss=16, step=2) == STRIDE
+    assert rp(ss=(1 << 32) // 128) == UNSUP
 
 
 def test_subblock_binding_checks_shapes_before_the_library():

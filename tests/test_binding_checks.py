@@ -126,3 +126,28 @@ def test_rope_positions_rows_and_reference(no_launch, monkeypatch):
     bare.positions = 0x2000
     with pytest.raises(ValueError, match="make_rope"):
         h3.h3f_qk_rmsnorm_rope3d(t(R, 2, 64), t(R, 2, 64), q, t(R, 2, 64), w, w, bare)
+
+
+def test_route_scores_layout():
+    # scores rows: dense, or the first nb columns of a [heads, nb, S] buffer; the
+    # helper returns the row stride the C call takes
+    heads, nb, keep = 3, 33, 7
+    kv = torch.zeros(heads, nb, keep, dtype=torch.int32)
+    assert h3._route_outputs(kv, t(heads, nb, nb), heads, nb, keep) == nb
+    assert h3._route_outputs(kv, t(heads, nb, 64)[:, :, :nb], heads, nb, keep) == 64
+    assert h3._route_outputs(kv[:1], t(1, nb, 40)[:, :, :nb], 1, nb, keep) == 40
+    with pytest.raises(ValueError, match="evenly spaced"):
+        h3._route_outputs(kv, t(heads, nb + 1, nb)[:, 1:], heads, nb, keep)   # head gap
+    with pytest.raises(ValueError, match="evenly spaced"):
+        h3._route_outputs(kv, t(heads, nb, nb).transpose(1, 2), heads, nb, keep)
+    with pytest.raises(ValueError, match="evenly spaced"):
+        h3._route_outputs(kv, t(heads, nb, 2 * nb)[:, :, ::2], heads, nb, keep)
+    with pytest.raises(ValueError, match=r"\[3, 33, 33\]"):
+        h3._route_outputs(kv, t(heads, nb, nb + 1), heads, nb, keep)
+    with pytest.raises(TypeError):
+        h3._route_outputs(kv, t(heads, nb, nb, dtype=bf16), heads, nb, keep)
+    with pytest.raises(ValueError, match="kv_blocks"):
+        h3._route_outputs(kv.transpose(0, 1).contiguous().transpose(0, 1), t(heads, nb, nb),
+                          heads, nb, keep)
+    v = h3.scores_view(heads, nb, "cpu")
+    assert v.shape == (heads, nb, nb) and v.stride() == (nb * 64, 64, 1)

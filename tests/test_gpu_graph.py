@@ -58,7 +58,7 @@ def _buffers():
         "q_out2": torch.empty(ROWS, H, Dh, dtype=torch.bfloat16, device=DEV),
         "k_out2": torch.empty(ROWS, H, Dh, dtype=torch.bfloat16, device=DEV),
         "kv2": torch.empty(H, nb, keep, dtype=torch.int32, device=DEV),
-        "scores2": torch.empty(H, nb, nb, dtype=torch.float32, device=DEV),
+        "scores2": h3.scores_view(H, nb, DEV),  # rows padded to 128 bytes
         "x": t["x"],
     }
     t["l1_ws"] = torch.empty(max(h3.h3f_residual_l1_workspace_bytes(ROWS, D, torch.bfloat16), 16),

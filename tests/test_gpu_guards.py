@@ -237,19 +237,24 @@ def test_residual_l1_out_guards(rows, D, dt):
 
 
 @pytest.mark.parametrize("rows,heads,block", [(4096 + 77, 3, 128), (4096, 5, 3)])
-def test_router_output_guards(rows, heads, block):
+@pytest.mark.parametrize("padded", [False, True], ids=["dense", "padded"])
+def test_router_output_guards(rows, heads, block, padded):
     q = dev_tensor("q", rows, heads * 128, "bf16").view(rows, heads, 128)
     k = dev_tensor("k", rows, heads * 128, "bf16").view(rows, heads, 128)
     nb, keep, _ = h3.h3f_subblock_plan(rows, heads, 128, block, 0.8, 10)
+    S = -(-nb // 32) * 32 + 3 if padded else nb  # rows of scores S floats apart
     pad = 1024
     kvbuf = torch.full((heads * nb * keep + 2 * pad,), -7, dtype=torch.int32, device=DEV)
-    scbuf = torch.full((heads * nb * nb + 2 * pad,), CANARY, dtype=torch.float32, device=DEV)
+    scbuf = torch.full((heads * nb * S + 2 * pad,), CANARY, dtype=torch.float32, device=DEV)
     kv = kvbuf[pad:pad + heads * nb * keep].view(heads, nb, keep)
-    sc = scbuf[pad:pad + heads * nb * nb].view(heads, nb, nb)
+    sc = scbuf[pad:pad + heads * nb * S].view(heads, nb, S)[:, :, :nb]
     h3.h3f_subblock_route(kv, sc, q, k, block, 0.8, 10)
     kb, sb = to_np(kvbuf), to_np(scbuf)
     assert (kb[:pad] == -7).all() and (kb[-pad:] == -7).all()
     assert (sb[:pad] == CANARY).all() and (sb[-pad:] == CANARY).all()
+    rows_of_sc = sb[pad:-pad].reshape(heads, nb, S)
+    assert (rows_of_sc[:, :, nb:] == CANARY).all()  # the pad columns of padded rows
+    assert not (rows_of_sc[:, :, :nb] == CANARY).any()  # every score written
     kvm = kb[pad:-pad]
     assert kvm.min() >= 0 and kvm.max() < nb  # every kept-list entry written
 

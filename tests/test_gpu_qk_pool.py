@@ -18,8 +18,9 @@ import torch
 import h3gen
 import oracle
 from gpu_util import DEV, dev_tensor, from_np, to_np
-from test_gpu_router import (assert_scores, block_abs_means, check_selection_on_own_scores,
-                             check_selection_valid, gamma, score_tol)
+from test_gpu_router import (PLAIN_FP32_MIN_BLOCK, assert_scores, block_abs_means,
+                             check_selection_on_own_scores, check_selection_valid, gamma,
+                             score_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -123,7 +124,8 @@ def test_qk_pool_outputs_and_means(case):
         kv, sc = to_np(kv), to_np(sc)
         kv_ref, sc_ref = oracle.subblock_route(qo_h, ko_h, block, sparsity, step)
         tol = score_tol(sc_ref, block_abs_means(qo_h, block), block_abs_means(ko_h, block), block)
-        assert_scores(sc, sc_ref, tol, f"pooled-route scores s={sparsity}")
+        assert_scores(sc, sc_ref, tol, f"pooled-route scores s={sparsity}",
+                      plain_fp32=block >= PLAIN_FP32_MIN_BLOCK)
         check_selection_on_own_scores(kv, sc)
         check_selection_valid(kv, sc_ref, tol)
 
@@ -152,9 +154,9 @@ def test_qk_pool_full_5s_shape():
     del qp, kp, q, k
     _, keep, _ = h3.h3f_subblock_plan(rows, heads, 128, block, 0.8, 10)
     kv = torch.empty(heads, nb, keep, dtype=torch.int32, device=DEV)
-    sc = torch.empty(heads, nb, nb, dtype=torch.float32, device=DEV)
+    sc = h3.scores_view(heads, nb, DEV)  # 128-byte rows, as the benchmark launches it
     h3.h3f_subblock_route_pooled(kv, sc, rows, heads, block, 0.8, 10, ws)
-    kv, sc = to_np(kv), to_np(sc)
+    kv, sc = to_np(kv), to_np(sc.contiguous())
     check_selection_on_own_scores(kv[::9], sc[::9])
     qblocks = np.array([0, 500, 977])
     for h in (0, 27):

@@ -9,7 +9,8 @@ and Stability of Numerical Algorithms", sec. 3.1, gamma_m = m u / (1 - m u),
 u = 2^-24): with a_q, a_k the block means of |q|, |k|,
   |err| <= 1e-6 + 1e-5 |ref| + (2 gamma_n + gamma_130) sum_d a_q[d] a_k[d],
 covering the rounding of each mean (gamma_n of the mean of |x|) and of the
-dot product of the rounded means.
+dot product of the rounded means.  Calls with blocks of 64 tokens or more (the
+5 s and 10 s shapes among them) are also held to the plain fp32 tolerance.
 The kept key blocks are an integer decision taken from floating point, where
 several answers can be right when two scores are within rounding of each
 other, so they are checked as follows:
@@ -64,15 +65,25 @@ def qk_tensors(rows, heads, packed=False, seed=0):
     return q, k, qh, kh
 
 
-def run_route(q, k, block, sparsity, step, sentinel=None):
+def padded_stride(nb):
+    """Score row stride of 128-byte rows, as the benchmark allocates them."""
+    return -(-nb // 32) * 32
+
+
+def run_route(q, k, block, sparsity, step, sentinel=None, stride=None, pad_out=None):
+    """kv, scores of one route call; scores rows `stride` floats apart (dense when
+    None).  pad_out (a list) receives the pad columns of padded rows."""
     rows, heads, _ = q.shape
     nb, keep, _ = h3.h3f_subblock_plan(rows, heads, 128, block, sparsity, step)
     kv = torch.full((heads, nb, keep), -7, dtype=torch.int32, device=DEV)
-    sc = torch.full((heads, nb, nb), float("nan") if sentinel is None else sentinel,
-                    dtype=torch.float32, device=DEV)
+    buf = torch.full((heads, nb, stride or nb), float("nan") if sentinel is None else sentinel,
+                     dtype=torch.float32, device=DEV)
+    sc = buf[:, :, :nb]
     h3.h3f_subblock_route(kv, sc, q, k, block, sparsity, step)
     torch.cuda.synchronize()
-    return to_np(kv), to_np(sc)
+    if pad_out is not None:
+        pad_out.append(to_np(buf[:, :, nb:].contiguous()))
+    return to_np(kv), to_np(sc.contiguous())
 
 
 def check_selection_on_own_scores(kv, sc):
@@ -118,6 +129,13 @@ def score_tol(ref, aq, ak, block):
     return FP32_ATOL + FP32_RTOL * np.abs(ref) + (2 * gamma(block) + gamma(130)) * (aq @ ak.transpose(0, 2, 1))
 
 
+# Blocks of at least this many tokens have block means well below 1 and scores
+# that also meet the plain fp32 output tolerance, which is then asserted too;
+# blocks of 1 - 3 tokens give O(10) scores formed with cancellation, held to
+# the derived bound alone.
+PLAIN_FP32_MIN_BLOCK = 64
+
+
 def assert_scores(sc, ref, tol, what, plain_fp32=False):
     """Scores within tol; with plain_fp32 also within the plain fp32 output tolerance."""
     err = np.abs(sc.astype(np.float64) - ref)
@@ -159,7 +177,7 @@ def test_router_matches_oracle(rows, heads, block, packed, sparsity):
     kv_ref, sc_ref = oracle.subblock_route(qh, kh, block, sparsity, 10)
     assert kv.shape == kv_ref.shape and sc.shape == sc_ref.shape
     tol = score_tol(sc_ref, block_abs_means(qh, block), block_abs_means(kh, block), block)
-    assert_scores(sc, sc_ref, tol, "block scores")
+    assert_scores(sc, sc_ref, tol, "block scores", plain_fp32=block >= PLAIN_FP32_MIN_BLOCK)
     check_selection_on_own_scores(kv, sc)
     check_selection_valid(kv, sc_ref, tol)
     agree = np.mean([len(np.intersect1d(a, b)) / kv.shape[2]
@@ -261,7 +279,7 @@ def test_router_full_10s_sampled():
     rows, heads, block = 61 * 48 * 84 + 256, 40, 128
     q = dev_tensor("q", rows, heads * 128, "bf16").view(rows, heads, 128)
     k = dev_tensor("k", rows, heads * 128, "bf16").view(rows, heads, 128)
-    kv, sc = run_route(q, k, block, 0.8, step=10)
+    kv, sc = run_route(q, k, block, 0.8, step=10, stride=padded_stride(1924))
     del q, k
     assert kv.shape == (40, 1924, 385)
     check_selection_on_own_scores(kv[::7], sc[::7])
@@ -287,7 +305,7 @@ def test_router_full_5s_sampled():
     rows, heads, block = 31 * 48 * 84 + 128, 40, 128
     q, k, _, _ = (dev_tensor("q", rows, heads * 128, "bf16").view(rows, heads, 128),
                   dev_tensor("k", rows, heads * 128, "bf16").view(rows, heads, 128), None, None)
-    kv, sc = run_route(q, k, block, 0.8, step=10)
+    kv, sc = run_route(q, k, block, 0.8, step=10, stride=padded_stride(978))
     assert kv.shape == (40, 978, 196)
     check_selection_on_own_scores(kv, sc)
     qblocks = np.array([0, 1, 500, 977])
@@ -303,6 +321,28 @@ def test_router_full_5s_sampled():
         # plain fp32 output tolerance
         assert_scores(sc[h, qblocks], ref, tol, f"scores head {h}", plain_fp32=True)
         check_selection_valid(kv[h, qblocks], ref, tol)
+
+
+@pytest.mark.parametrize("rows,heads,block", [
+    (4096 + 77, 3, 128),   # 33 blocks (odd: 4- and 8-byte stores at the row end)
+    (4096, 2, 3),          # 1366 blocks (2 mod 4)
+    (4096, 8, 64),         # 64 blocks (whole 16-byte groups)
+], ids=["nb33", "nb1366", "nb64"])
+@pytest.mark.parametrize("extra", [0, 5], ids=["rows128B", "rows-odd"])
+def test_router_padded_score_rows(rows, heads, block, extra):
+    # scores rows further apart than n_blocks: the same scores (bit for bit) and
+    # kept lists as dense rows, and the pad columns are never written; extra = 5
+    # makes a stride that is not a multiple of 4 (rows only 4-byte aligned)
+    q, k, _, _ = qk_tensors(rows, heads, seed=4)
+    nb, _, _ = h3.h3f_subblock_plan(rows, heads, 128, block, 0.8, 10)
+    kv_d, sc_d = run_route(q, k, block, 0.8, 10)
+    pads = []
+    kv_p, sc_p = run_route(q, k, block, 0.8, 10, sentinel=-7.0, stride=padded_stride(nb) + extra,
+                           pad_out=pads)
+    assert np.array_equal(sc_p.view(np.uint32), sc_d.view(np.uint32))
+    assert np.array_equal(kv_p, kv_d)
+    assert pads[0].size == heads * nb * (padded_stride(nb) + extra - nb)
+    assert (pads[0] == -7.0).all(), "a pad column of the scores was written"
 
 
 def test_router_maximum_blocks():

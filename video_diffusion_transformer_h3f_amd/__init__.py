@@ -98,14 +98,14 @@ def lib():
         L.h3f_subblock_plan.argtypes = [i64, i32, i32, i32, ctypes.c_double, i32,
                                         ctypes.POINTER(i32), ctypes.POINTER(i32),
                                         ctypes.POINTER(ctypes.c_size_t)]
-        L.h3f_subblock_route.argtypes = [p, p, p, i64, i64, p, i64, i64, st, i64, i32, i32, i32,
-                                         ctypes.c_double, i32, p, ctypes.c_size_t, p]
+        L.h3f_subblock_route.argtypes = [p, p, i64, p, i64, i64, p, i64, i64, st, i64, i32, i32,
+                                         i32, ctypes.c_double, i32, p, ctypes.c_size_t, p]
         L.h3f_qk_rmsnorm_rope3d_pool.argtypes = [p, i64, i64, p, i64, i64, p, i64, i64, p, i64,
                                                  i64, p, p, st, i64, i32, i32, f,
                                                  ctypes.POINTER(Rope3D), i32, p, ctypes.c_size_t,
                                                  p]
-        L.h3f_subblock_route_pooled.argtypes = [p, p, i64, i32, i32, i32, ctypes.c_double, i32, p,
-                                                ctypes.c_size_t, p]
+        L.h3f_subblock_route_pooled.argtypes = [p, p, i64, i64, i32, i32, i32, ctypes.c_double,
+                                                i32, p, ctypes.c_size_t, p]
         _lib = L
     return _lib
 
@@ -371,22 +371,44 @@ def h3f_qk_rmsnorm_rope3d_pool(q_out, k_out, q, k, q_weight, k_weight, rope: Rop
     return q_out, k_out
 
 
+def _route_outputs(kv_blocks, scores, heads, nb, keep):
+    """Checks the router's outputs and returns the row stride of scores in floats:
+    kv_blocks int32 [heads, nb, keep] contiguous; scores float32 [heads, nb, nb]
+    whose rows are evenly spaced, dense or the first nb columns of a contiguous
+    [heads, nb, S] buffer (S a multiple of 32 lets the kernel write whole lines)."""
+    import torch
+
+    if kv_blocks.dtype != torch.int32 or scores.dtype != torch.float32:
+        raise TypeError("kv_blocks must be int32 and scores float32")
+    if tuple(kv_blocks.shape) != (heads, nb, keep) or tuple(scores.shape) != (heads, nb, nb):
+        raise ValueError(f"kv_blocks must be [{heads}, {nb}, {keep}] and scores [{heads}, {nb}, {nb}]")
+    if not kv_blocks.is_contiguous():
+        raise ValueError("kv_blocks must be contiguous")
+    s0, s1, s2 = scores.stride()
+    if s2 != 1 or s1 < nb or (heads > 1 and s0 != nb * s1):
+        raise ValueError("scores rows must be evenly spaced: strides (nb * S, S, 1) with S >= nb")
+    return s1
+
+
+def scores_view(heads: int, n_blocks: int, device, pad_to: int = 32):
+    """A float32 [heads, n_blocks, n_blocks] view for the router's scores whose rows
+    are padded to a multiple of pad_to floats (32: 128-byte rows, each line of
+    scores written whole).  The pad columns are never written."""
+    import torch
+
+    s = -(-n_blocks // pad_to) * pad_to
+    return torch.empty(heads, n_blocks, s, dtype=torch.float32, device=device)[:, :, :n_blocks]
+
+
 def h3f_subblock_route_pooled(kv_blocks, scores, rows: int, heads: int, block: int,
                               sparsity: float, step: int, workspace, stream=None):
     """Router score + selection from the block means h3f_qk_rmsnorm_rope3d_pool wrote
     into `workspace`; kv_blocks / scores as for h3f_subblock_route."""
-    import torch
-
     dev = _dev(kv_blocks, scores, workspace)
-    if kv_blocks.dtype != torch.int32 or scores.dtype != torch.float32:
-        raise TypeError("kv_blocks must be int32 and scores float32")
-    if not (kv_blocks.is_contiguous() and scores.is_contiguous()):
-        raise ValueError("kv_blocks and scores must be contiguous")
     nb, keep, _ = h3f_subblock_plan(rows, heads, 128, block, sparsity, step)
-    if tuple(kv_blocks.shape) != (heads, nb, keep) or tuple(scores.shape) != (heads, nb, nb):
-        raise ValueError(f"kv_blocks must be [{heads}, {nb}, {keep}] and scores [{heads}, {nb}, {nb}]")
+    srs = _route_outputs(kv_blocks, scores, heads, nb, keep)
     _check("h3f_subblock_route_pooled", lib().h3f_subblock_route_pooled(
-        _ptr(kv_blocks), _ptr(scores), rows, heads, 128, block, float(sparsity), step,
+        _ptr(kv_blocks), _ptr(scores), srs, rows, heads, 128, block, float(sparsity), step,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev, stream)))
     return kv_blocks, scores
 
@@ -507,9 +529,10 @@ def h3f_subblock_plan(rows: int, heads: int, head_dim: int, block: int, sparsity
 def h3f_subblock_route(kv_blocks, scores, q, k, block: int, sparsity: float, step: int,
                        workspace=None, stream=None):
     """Block-sparse attention router.  q, k: bf16 [rows, heads, head_dim] views;
-    kv_blocks: int32 [heads, n_blocks, keep]; scores: float32 [heads, n_blocks,
-    n_blocks] (both contiguous; sizes from h3f_subblock_plan).  workspace: uint8
-    GPU tensor of at least the planned bytes; allocated here (torch) when None."""
+    kv_blocks: int32 [heads, n_blocks, keep], contiguous; scores: float32 [heads,
+    n_blocks, n_blocks], dense or padded rows (scores_view); sizes from
+    h3f_subblock_plan.  workspace: uint8 GPU tensor of at least the planned bytes;
+    allocated here (torch) when None."""
     import torch
 
     dev = _dev(kv_blocks, scores, q, k)
@@ -518,17 +541,12 @@ def h3f_subblock_route(kv_blocks, scores, q, k, block: int, sparsity: float, ste
     if shp != kshp:
         raise ValueError("q and k shapes differ")
     rows, heads, head_dim = shp
-    if kv_blocks.dtype != torch.int32 or scores.dtype != torch.float32:
-        raise TypeError("kv_blocks must be int32 and scores float32")
-    if not (kv_blocks.is_contiguous() and scores.is_contiguous()):
-        raise ValueError("kv_blocks and scores must be contiguous")
     nb, keep, need = h3f_subblock_plan(rows, heads, head_dim, block, sparsity, step)
-    if tuple(kv_blocks.shape) != (heads, nb, keep) or tuple(scores.shape) != (heads, nb, nb):
-        raise ValueError(f"kv_blocks must be [{heads}, {nb}, {keep}] and scores [{heads}, {nb}, {nb}]")
+    srs = _route_outputs(kv_blocks, scores, heads, nb, keep)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _check("h3f_subblock_route", lib().h3f_subblock_route(
-        _ptr(kv_blocks), _ptr(scores), _ptr(q), qrs, qhs, _ptr(k), krs, khs, _dtype(q), rows,
+        _ptr(kv_blocks), _ptr(scores), srs, _ptr(q), qrs, qhs, _ptr(k), krs, khs, _dtype(q), rows,
         heads, head_dim, block, float(sparsity), step, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(dev, stream)))
     return kv_blocks, scores

@@ -234,9 +234,10 @@ constexpr int kWaveTile = 32;   // per wave: 2 x 2 MFMA tiles of 16 x 16
 
 struct ScoreArgs {
     const float* pooled;  // [2][heads][nb][128]
-    float* scores;        // [heads][nb][nb]
+    float* scores;        // [heads][nb][ss], the first nb columns of each row
     int32_t heads;
     uint32_t nb;
+    uint32_t ss;          // row stride of scores in floats (>= nb)
     uint32_t tiles;       // ceil(nb / 64)
 };
 
@@ -303,15 +304,15 @@ constexpr uint32_t kScoreRun = H3F_SCORE_RUN;  // column tiles per workgroup
 constexpr uint32_t kDropped = 0xFFFFFFF0u;
 
 template <int SB>
-__device__ __forceinline__ void store_tile32_t(rsrc_t r, uint32_t nb, uint32_t i0, uint32_t j0,
-                                               int ri, int g, const f32x4 (&acc)[2][2]) {
+__device__ __forceinline__ void store_tile32_t(rsrc_t r, uint32_t nb, uint32_t ss, uint32_t i0,
+                                               uint32_t j0, int ri, int g, const f32x4 (&acc)[2][2]) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         const uint32_t i = i0 + 16 * m + ri;
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const uint32_t j = j0 + 16 * n + 4 * g;
-            const uint32_t off = (i * nb + j) * 4u;
+            const uint32_t off = (i * ss + j) * 4u;
             const f32x4 v = acc[m][n];
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r,
                                                    i < nb && j + 3 < nb ? off : kDropped, 0, 0);
@@ -366,7 +367,7 @@ __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
     const uint32_t mat_bytes = a.nb * kHeadDim * 4u;
     const rsrc_t rq = make_rsrc(a.pooled + (size_t)h * a.nb * kHeadDim, mat_bytes);
     const rsrc_t rk = make_rsrc(a.pooled + ((size_t)a.heads + h) * a.nb * kHeadDim, mat_bytes);
-    const rsrc_t ro = make_rsrc(a.scores + (size_t)h * a.nb * a.nb, a.nb * a.nb * 4u);
+    const rsrc_t ro = make_rsrc(a.scores + (size_t)h * a.nb * a.ss, a.nb * a.ss * 4u);
 
     // step s = 2 t + hk: half hk of key tile t.  Wavefront w gathers fragments
     // 4 w .. 4 w + 3 of it into buffer b; fragment f = 4 R + v' holds rows
@@ -432,7 +433,7 @@ __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
                     acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(B[n][kk], A[m][16 * hk + kk],
                                                                      acc[m][n], 0, 0, 0);
         if (hk == 1)
-            store_tile32_t<SB>(ro, a.nb, i0,
+            store_tile32_t<SB>(ro, a.nb, a.ss, i0,
                                jrun + (uint32_t)(s >> 1) * kTile + (wave & 1) * kWaveTile, ri, g,
                                acc);
     }
@@ -444,10 +445,11 @@ __global__ void __launch_bounds__(256) subblock_score_kernel(ScoreArgs a) {
 constexpr int kSelWaves = 4;  // rows per workgroup, one wavefront each
 
 struct SelectArgs {
-    const float* scores;  // [heads][nb][nb]
+    const float* scores;  // [heads][nb][ss]
     int32_t* kv;          // [heads][nb][keep]
     uint32_t rows;        // heads * nb
     uint32_t nb;
+    uint32_t ss;          // row stride of scores in floats
     uint32_t keep;
     float z;  // first probe at mean + z * std of the row (z: normal quantile of the kept share)
 };
@@ -519,7 +521,7 @@ __global__ void __launch_bounds__(64 * kSelWaves) subblock_select_kernel(SelectA
     const uint32_t lane = threadIdx.x & 63;
     // All KPL loads are issued before any is used: a buffer resource over the
     // row returns 0 past its end, so no load sits behind a branch.
-    const rsrc_t rs = make_rsrc(a.scores + (size_t)row * a.nb, a.nb * 4u);
+    const rsrc_t rs = make_rsrc(a.scores + (size_t)row * a.ss, a.nb * 4u);
     uint32_t sv[KPL];  // raw fp32 bits
 #pragma unroll
     for (int m = 0; m < KPL; ++m)
@@ -680,14 +682,25 @@ h3f_status_t check_plan(int64_t rows, int32_t heads, int32_t head_dim, int32_t b
     return H3F_OK;
 }
 
+// Rows of scores lie scores_row_stride >= n_blocks floats apart, and one
+// head's matrix is addressed with 32-bit byte offsets that must stay below
+// the offset that marks a dropped store.
+h3f_status_t check_scores_stride(int64_t nb, int64_t scores_row_stride) {
+    if (scores_row_stride < nb) return H3F_ERR_BAD_STRIDE;
+    if (scores_row_stride > (int64_t)kDropped / (4 * nb)) return H3F_ERR_UNSUPPORTED;
+    return H3F_OK;
+}
+
 // Block scores from the pooled means, then the kept lists (routed steps).
-void launch_score_select(const float* pooled, float* scores, int32_t* kv_blocks, int32_t heads,
-                         int64_t nb, int64_t keep, hipStream_t s) {
+void launch_score_select(const float* pooled, float* scores, int64_t scores_row_stride,
+                         int32_t* kv_blocks, int32_t heads, int64_t nb, int64_t keep,
+                         hipStream_t s) {
     ScoreArgs sa;
     sa.pooled = pooled;
     sa.scores = scores;
     sa.heads = heads;
     sa.nb = (uint32_t)nb;
+    sa.ss = (uint32_t)scores_row_stride;
     sa.tiles = (uint32_t)((nb + kTile - 1) / kTile);
     const dim3 scg((unsigned)(heads * sa.tiles * ((sa.tiles + kScoreRun - 1) / kScoreRun)));
     if (nb % 4 == 0)
@@ -702,6 +715,7 @@ void launch_score_select(const float* pooled, float* scores, int32_t* kv_blocks,
     se.kv = kv_blocks;
     se.rows = (uint32_t)(heads * nb);
     se.nb = (uint32_t)nb;
+    se.ss = (uint32_t)scores_row_stride;
     se.keep = (uint32_t)keep;
     se.z = normal_upper_quantile((double)keep / (double)nb);
     const dim3 sg((se.rows + kSelWaves - 1) / kSelWaves), sb(64 * kSelWaves);
@@ -743,7 +757,8 @@ extern "C" h3f_status_t h3f_subblock_plan(int64_t rows, int32_t heads, int32_t h
     return H3F_OK;
 }
 
-extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, const void* q,
+extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores,
+                                           int64_t scores_row_stride, const void* q,
                                            int64_t q_row_stride, int64_t q_head_stride,
                                            const void* k, int64_t k_row_stride,
                                            int64_t k_head_stride, h3f_dtype_t dtype, int64_t rows,
@@ -789,12 +804,14 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
 
     const int64_t nb = ceil_div(rows, block);
     const int64_t keep = keep_for(nb, sparsity, step);
+    const h3f_status_t sst = check_scores_stride(nb, scores_row_stride);
+    if (sst != H3F_OK) return sst;
     const size_t need = workspace_for(nb, heads);
     const bool routed = step >= H3F_SUBBLOCK_FIRST_STEP;
     if (routed && (!workspace || !aligned16(workspace) || workspace_bytes < need))
         return H3F_ERR_WORKSPACE;
     const Region rkv = region2d(kv_blocks, 1, 0, (int64_t)heads * nb * keep * 4, 1);
-    const Region rsc = region2d(scores, 1, 0, (int64_t)heads * nb * nb * 4, 1);
+    const Region rsc = region2d(scores, (int64_t)heads * nb, scores_row_stride, nb, 4);
     const Region rws = region2d(workspace, 1, 0, routed ? (int64_t)need : 0, 1);
     if (!disjoint(rkv, rq) || !disjoint(rkv, rk) || !disjoint(rkv, rws) ||
         (routed && (!disjoint(rkv, rsc) || !disjoint(rsc, rq) || !disjoint(rsc, rk) ||
@@ -844,11 +861,12 @@ extern "C" h3f_status_t h3f_subblock_route(int32_t* kv_blocks, float* scores, co
                            dim3(2 * pa.n_blocks * pa.n_groups), dim3(64 * kPoolWaves), 0, s, pa);
     }
 
-    launch_score_select(pa.pooled, scores, kv_blocks, heads, nb, keep, s);
+    launch_score_select(pa.pooled, scores, scores_row_stride, kv_blocks, heads, nb, keep, s);
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }
 
-extern "C" h3f_status_t h3f_subblock_route_pooled(int32_t* kv_blocks, float* scores, int64_t rows,
+extern "C" h3f_status_t h3f_subblock_route_pooled(int32_t* kv_blocks, float* scores,
+                                                  int64_t scores_row_stride, int64_t rows,
                                                   int32_t heads, int32_t head_dim, int32_t block,
                                                   double sparsity, int32_t step,
                                                   const void* workspace, size_t workspace_bytes,
@@ -860,17 +878,20 @@ extern "C" h3f_status_t h3f_subblock_route_pooled(int32_t* kv_blocks, float* sco
     if (reinterpret_cast<uintptr_t>(kv_blocks) & 3u) return H3F_ERR_MISALIGNED;
     const int64_t nb = ceil_div(rows, block);
     const int64_t keep = keep_for(nb, sparsity, step);
+    const h3f_status_t sst = check_scores_stride(nb, scores_row_stride);
+    if (sst != H3F_OK) return sst;
     const size_t need = workspace_for(nb, heads);
     const bool routed = step >= H3F_SUBBLOCK_FIRST_STEP;
     if (routed && (!workspace || !aligned16(workspace) || workspace_bytes < need))
         return H3F_ERR_WORKSPACE;
     const Region rkv = region2d(kv_blocks, 1, 0, (int64_t)heads * nb * keep * 4, 1);
-    const Region rsc = region2d(scores, 1, 0, (int64_t)heads * nb * nb * 4, 1);
+    const Region rsc = region2d(scores, (int64_t)heads * nb, scores_row_stride, nb, 4);
     const Region rws = region2d(workspace, 1, 0, routed ? (int64_t)need : 0, 1);
     if (!disjoint(rkv, rws) || (routed && (!disjoint(rkv, rsc) || !disjoint(rsc, rws))))
         return H3F_ERR_ALIASING;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!routed) return launch_dense(kv_blocks, heads, nb, keep, s);
-    launch_score_select(static_cast<const float*>(workspace), scores, kv_blocks, heads, nb, keep, s);
+    launch_score_select(static_cast<const float*>(workspace), scores, scores_row_stride, kv_blocks,
+                        heads, nb, keep, s);
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }
