@@ -54,6 +54,29 @@ MUTANTS = {
                                  "if (a->score > b->score) return 1;\n    if (a->score < b->score) return -1;"),
     "subblock_ties_higher_index": ("return (a->block > b->block) - (a->block < b->block);",
                                    "return (a->block < b->block) - (a->block > b->block);"),
+    "group_by_modulo": ("return rows_per_group > 0 ? r / rows_per_group : 0;",
+                        "return rows_per_group > 0 ? r % rows_per_group : 0;"),
+    "residual_l1_den_of_cur": ("den += fabs(p);", "den += fabs(c);"),
+    "residual_l1_squared": ("num += fabs(c - p);", "num += (c - p) * (c - p);"),
+    "fused_ln_before_residual": (
+        "gated_row(x, x_dtype, h, h_dtype, gate, r, g, hidden);\n"
+        "        adaln_row(y, y_dtype, x, x_dtype, shift, scale, x_dtype, r, g, hidden,\n"
+        "                  (double)eps);",
+        "adaln_row(y, y_dtype, x, x_dtype, shift, scale, x_dtype, r, g, hidden,\n"
+        "                  (double)eps);\n"
+        "        gated_row(x, x_dtype, h, h_dtype, gate, r, g, hidden);"),
+    "positions_offset_ignored": ("int64_t p = (token_offset + r) % L;", "int64_t p = r % L;"),
+    "rope_chunk_start_fixed": ("start += dc;", "start += 0;"),
+    "subblock_kept_unsorted": ("qsort(out, (size_t)keep, sizeof *out, by_index_asc);",
+                               "(void)by_index_asc;"),
+    "gated_gate_in_h_dtype": ("const double gv = ld(gate, x_dtype, g * D + c);",
+                              "const double gv = ld(gate, h_dtype, g * D + c);"),
+    "affine_drop_eps": ("const double sigma = sqrt(ss / (double)D + eps);",
+                        "const double sigma = sqrt(ss / (double)D);"),
+    "subblock_scores_half_dot": ("for (int32_t d = 0; d < head_dim; ++d) s += a[d] * c[d];",
+                                 "for (int32_t d = 0; d < head_dim / 2; ++d) s += a[d] * c[d];"),
+    "rope_exact_angle_exponent": ("phi = (double)p3[c] * pow(theta, -2.0 * (double)j / (double)dc);",
+                                  "phi = (double)p3[c] * pow(theta, -1.0 * (double)j / (double)dc);"),
 }
 
 

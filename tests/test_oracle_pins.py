@@ -247,6 +247,18 @@ def test_gated_bf16_unit_gate_is_rounded_sum():
     assert np.array_equal(got, bf16_bits(s))
 
 
+def test_gated_fp32_stream_bf16_branch():
+    # the chain's mixed form: fp32 stream, bf16 branch output, fp32 gate.  Every
+    # bf16 value is exact in fp32, so x = 0 with gate = 1 leaves x = h exactly,
+    # and x = -h/2 with gate = 1/2 leaves exactly 0
+    hb = bf16_bits(RNG.standard_normal((6, 64)))
+    h = as_f64(hb)
+    got = oracle.gated_residual(f32(np.zeros((6, 64))), hb, f32(np.ones((1, 64))))
+    assert np.array_equal(got, f32(h))
+    got = oracle.gated_residual(f32(-h / 2), hb, f32(np.full((1, 64), 0.5)))
+    assert np.array_equal(got, f32(np.zeros((6, 64))))
+
+
 def test_gated_linear_in_gate_and_h():
     x = f32(np.zeros((4, 64)))
     h = f32(RNG.integers(-64, 64, (4, 64)) / 16.0)
