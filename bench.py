@@ -58,6 +58,9 @@ for _D, _F in ((3072, 8320), (4096, 11008), (5120, 13824), (6144, 16640)):
     GRIDS[f"sweep{_D}"] = dict(T=8, H=48, W=84, A=512, D=_D, heads=_D // 128, Dh=128,
                                split=(32, 48, 48), F=_F)
 
+# the small parity configuration (fp32 throughout), timed on the oracle only
+TINY = dict(T=2, H=6, W=8, A=16, D=256, heads=4, Dh=64, split=(16, 24, 24), F=512)
+
 CHAIN_STEPS = 50  # the chain workload's step count (one DiT block epilogue per denoising step)
 
 
@@ -90,19 +93,20 @@ def n_tokens(c):
     return c["T"] * c["H"] * c["W"] + c["A"]
 
 
-def op_bytes(name, N, c, x_bytes=2):
-    """Algorithmic bytes of one call (activations bf16, x of x_bytes per element)."""
+def op_bytes(name, N, c, x_bytes=2, a=2):
+    """Algorithmic bytes of one call (activations of `a` bytes per element, bf16
+    by default; x and its modulation of x_bytes)."""
     D, F, H, Dh = c["D"], c["F"], c["heads"], c["Dh"]
     if name == "adaln":
-        return N * D * x_bytes + N * D * 2 + 2 * D * x_bytes
+        return N * D * x_bytes + N * D * a + 2 * D * x_bytes
     if name == "gated":
-        return 2 * N * D * x_bytes + N * D * 2 + D * x_bytes
+        return 2 * N * D * x_bytes + N * D * a + D * x_bytes
     if name == "swiglu":
-        return 3 * N * F * 2
+        return 3 * N * F * a
     if name == "qk":
-        return 4 * N * H * Dh * 2 + 2 * Dh * 2
+        return 4 * N * H * Dh * a + 2 * Dh * a
     if name == "gated_adaln":
-        return 2 * N * D * x_bytes + N * D * 2 + N * D * 2 + 3 * D * x_bytes
+        return 2 * N * D * x_bytes + N * D * a + N * D * a + 3 * D * x_bytes
     raise KeyError(name)
 
 
@@ -396,17 +400,17 @@ def time_extra_ops(args, torch, h3, h3gen, dev, c, t, rope, K, per_op):
     return out
 
 
-def cpu_baseline(c, rows, x_bytes, min_seconds=10.0, seed=0):
+def cpu_baseline(c, rows, x_bytes, min_seconds=10.0, seed=0, act="bf16"):
     """Time the oracle on `rows` rows of the same workload (one block's six calls),
     on all the host threads it uses, and again on one thread over a sixteenth of
     the sample."""
     import oracle
 
-    full = _time_oracle(c, rows, x_bytes, min_seconds, seed)
+    full = _time_oracle(c, rows, x_bytes, min_seconds, seed, act)
     threads = oracle.num_threads()
     oracle.set_num_threads(1)
     try:
-        one = _time_oracle(c, max(1, rows // 16), x_bytes, min_seconds / 2, seed)
+        one = _time_oracle(c, max(1, rows // 16), x_bytes, min_seconds / 2, seed, act)
     finally:
         oracle.set_num_threads(threads)
     full["single_thread"] = {"value": one["value"], "unit": "GB/s", "cores": 1,
@@ -415,7 +419,7 @@ def cpu_baseline(c, rows, x_bytes, min_seconds=10.0, seed=0):
     return full
 
 
-def _time_oracle(c, rows, x_bytes, min_seconds, seed):
+def _time_oracle(c, rows, x_bytes, min_seconds, seed, act="bf16"):
     import numpy as np
 
     import h3gen
@@ -423,7 +427,9 @@ def _time_oracle(c, rows, x_bytes, min_seconds, seed):
 
     D, F, H, Dh = c["D"], c["F"], c["heads"], c["Dh"]
     xd = "f32" if x_bytes == 4 else "bf16"
-    g = lambda n, r, cols, dt="bf16": h3gen.host_rows(n, r, cols, dt, seed=seed)  # noqa: E731
+    y_dt = np.uint16 if act == "bf16" else np.float32
+    a = 2 if act == "bf16" else 4
+    g = lambda n, r, cols, dt=act: h3gen.host_rows(n, r, cols, dt, seed=seed)  # noqa: E731
     x = g("x", rows, D, xd)
     mods = {n: g(n, 1, D, xd) for n in ("shift", "scale", "gate", "shift2", "scale2", "gate2")}
     hh, hh2 = g("h", rows, D), g("h2", rows, D)
@@ -439,17 +445,17 @@ def _time_oracle(c, rows, x_bytes, min_seconds, seed):
     t0 = time.perf_counter()
     while True:
         x = x0
-        oracle.adaln_modulate(x, mods["shift"], mods["scale"], y_dtype=np.uint16)
+        oracle.adaln_modulate(x, mods["shift"], mods["scale"], y_dtype=y_dt)
         oracle.qk_rmsnorm_rope3d(q, k, qw, kw, pos, c["split"])
         x = oracle.gated_residual(x, hh, mods["gate"])
-        oracle.adaln_modulate(x, mods["shift2"], mods["scale2"], y_dtype=np.uint16)
+        oracle.adaln_modulate(x, mods["shift2"], mods["scale2"], y_dtype=y_dt)
         oracle.swiglu(gu)
         oracle.gated_residual(x, hh2, mods["gate2"])
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
-    nbytes = reps * sum(op_bytes(n, rows, c, x_bytes) for n in
+    nbytes = reps * sum(op_bytes(n, rows, c, x_bytes, a) for n in
                         ("adaln", "qk", "gated", "adaln", "swiglu", "gated"))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(dt, 3), "steps": reps,
@@ -537,9 +543,15 @@ def main():
     # ---- oracle leg (after every timed region): CPU baseline and output check ----
     from bench_check import check_block_step
 
-    cpu = None
+    cpu, oracle_tiny = None, None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(c, min(args.cpu_rows, N), x_bytes, seed=args.seed)
+        if extras:
+            # the small parity configuration on full tensors (fp32 throughout)
+            oracle_tiny = cpu_baseline(TINY, n_tokens(TINY), 4, min_seconds=2.0, seed=args.seed,
+                                       act="f32")
+            oracle_tiny["config"] = ("tiny: 112 tokens (2x6x8 video + 16 audio), hidden 256, "
+                                     "4x64 heads, SwiGLU inner 512, fp32 throughout")
         if "chain10s" in extra_workloads:
             # the oracle on the chain's own form (fp32 residual stream, 10 s grid)
             extra_workloads["chain10s"]["cpu_baseline"] = _time_oracle(
@@ -597,6 +609,7 @@ def main():
         "wall_s_timed_region": head["wall_s_timed_region"],
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "oracle_tiny": oracle_tiny,
     }
     print(json.dumps(out), flush=True)
     if not check["ok"]:

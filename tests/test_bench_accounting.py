@@ -67,3 +67,18 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "exactly one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("op,per_token,vectors", [
+    ("adaln", 2 * 256 * 4, 2 * 256 * 4),
+    ("gated", 3 * 256 * 4, 256 * 4),
+    ("swiglu", 3 * 512 * 4, 0),
+    ("qk", 4 * 4 * 64 * 4, 2 * 64 * 4),
+    ("gated_adaln", 4 * 256 * 4, 3 * 256 * 4),
+])
+def test_per_token_bytes_tiny_fp32(op, per_token, vectors):
+    # the tiny configuration: 112 tokens, hidden 256, 4 x 64 heads, SwiGLU inner
+    # 512, every tensor fp32
+    n = bench.n_tokens(bench.TINY)
+    assert n == 2 * 6 * 8 + 16 == 112
+    assert bench.op_bytes(op, n, bench.TINY, 4, 4) == n * per_token + vectors
