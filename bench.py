@@ -267,7 +267,8 @@ def measure_references(torch, h3, dev):
     """Bandwidth references on 2 GiB buffers (10 launches each after 3 warmups):
     the library's streaming copy, hipMemcpyDtoD (torch copy_ of a contiguous
     device tensor), a read-only stream (streaming and cached loads) and a
-    write-only stream."""
+    write-only stream, the latter also with each wavefront storing 1, 2, 5 or 10
+    KiB before it ends (a row-holding kernel stores its whole row)."""
     nb = 2 << 30
     src = torch.empty(nb, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -291,6 +292,9 @@ def measure_references(torch, h3, dev):
         "read_only_GBps": rate(lambda: h3.h3f_stream_read(src, sink), nb),
         "read_only_cached_GBps": rate(lambda: h3.h3f_stream_read(src, sink, cached=True), nb),
         "write_only_GBps": rate(lambda: h3.h3f_stream_fill(dst, 0x3F803F80), nb),
+        "write_only_by_kib_per_wavefront_GBps": {
+            str(k): rate(lambda: h3.h3f_stream_fill_bursts(dst, k, 0x3F803F80), nb)
+            for k in (1, 2, 5, 10)},
     }
     ref["best_copy_GBps"] = max(ref["stream_copy_GBps"], ref["hipMemcpyDtoD_GBps"])
     ref["note"] = ("2 GiB each way; copies count read + write bytes, the one-direction "

@@ -408,6 +408,18 @@ h3f_status_t h3f_stream_read(const void* src, int64_t bytes, int32_t cached, voi
                              void* stream);
 h3f_status_t h3f_stream_fill(void* dst, int64_t bytes, uint32_t value, void* stream);
 
+/*
+ * The write-only stream in store bursts (measurement helper): as
+ * h3f_stream_fill, but each 64-wide wavefront writes its own contiguous
+ * kib_per_wavefront KiB (1, 2, 5 or 10) with 16-byte streaming stores before it
+ * ends, wavefronts in address order.  It measures what a wavefront that stores
+ * several KiB can write, the pattern of kernels that hold a whole row (a 10 KiB
+ * row at hidden 5120 in bf16) between their loads and stores.  Errors as
+ * h3f_stream_fill; H3F_ERR_UNSUPPORTED for another kib_per_wavefront.
+ */
+h3f_status_t h3f_stream_fill_bursts(void* dst, int64_t bytes, uint32_t value,
+                                    int32_t kib_per_wavefront, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -236,6 +236,13 @@ def test_stream_read_and_fill_validation():
     assert L.h3f_stream_fill(None, 16, 7, None) == NULLP
     assert L.h3f_stream_fill(A(0), 24, 7, None) == SHAPE
     assert L.h3f_stream_fill(P(0x10000004), 32, 7, None) == MISAL
+    assert L.h3f_stream_fill_bursts(None, 0, 7, 10, None) == OK
+    assert L.h3f_stream_fill_bursts(None, 16, 7, 10, None) == NULLP
+    assert L.h3f_stream_fill_bursts(A(0), 24, 7, 10, None) == SHAPE
+    assert L.h3f_stream_fill_bursts(A(0), -16, 7, 10, None) == SHAPE
+    assert L.h3f_stream_fill_bursts(P(0x10000004), 32, 7, 10, None) == MISAL
+    for k in (0, 3, 4, 11, -1):
+        assert L.h3f_stream_fill_bursts(A(0), 1 << 20, 7, k, None) == UNSUP
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

@@ -224,6 +224,21 @@ def test_qk_packed_in_place_guards(rows, heads):
     assert_close(to_np(k), rk, "bf16", "k in place")
 
 
+
+@pytest.mark.parametrize("kib", [1, 2, 5, 10])
+@pytest.mark.parametrize("nbytes", [16, 4096 * 10 - 16, 3 * 40960 + 1008, 1 << 20])
+def test_stream_fill_bursts_writes_exactly_its_bytes(kib, nbytes):
+    # every 32-bit word of [0, nbytes) takes the value, nothing past it changes
+    # (ragged last wavefront, a part-filled last workgroup, a single chunk)
+    pad = 4096
+    buf = torch.full((nbytes // 4 + 2 * pad,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    view = buf[pad:pad + nbytes // 4]
+    h3.h3f_stream_fill_bursts(view, kib, value=0x12345678)
+    b = to_np(buf)
+    assert (b[:pad] == 0x5A5A5A5A).all() and (b[pad + nbytes // 4:] == 0x5A5A5A5A).all()
+    assert (b[pad:pad + nbytes // 4] == 0x12345678).all()
+
+
 @pytest.mark.parametrize("rows,D,dt", [(1, 8, "bf16"), (1001, 5120, "bf16"), (67, 1000, "f32")])
 def test_residual_l1_out_guards(rows, D, dt):
     buf = torch.full((16,), CANARY, dtype=torch.float64, device=DEV)

@@ -36,7 +36,8 @@ EXPORTS = [
     "h3f_stream_copy", "h3f_residual_l1_workspace_bytes", "h3f_residual_l1",
     "h3f_subblock_plan", "h3f_subblock_route", "h3f_adaln_affine_modulate",
     "h3f_qk_rmsnorm_rope3d_pool", "h3f_subblock_route_pooled", "h3f_stream_read",
-    "h3f_stream_fill", "h3f_residual_l1_noalloc", "h3f_residual_l1_noalloc_max_bytes",
+    "h3f_stream_fill", "h3f_stream_fill_bursts", "h3f_residual_l1_noalloc",
+    "h3f_residual_l1_noalloc_max_bytes",
 ]
 
 
@@ -87,6 +88,7 @@ def lib():
         L.h3f_stream_copy.argtypes = [p, p, i64, p]
         L.h3f_stream_read.argtypes = [p, i64, i32, p, p]
         L.h3f_stream_fill.argtypes = [p, i64, ctypes.c_uint32, p]
+        L.h3f_stream_fill_bursts.argtypes = [p, i64, ctypes.c_uint32, i32, p]
         L.h3f_residual_l1.argtypes = [p, p, i64, p, i64, st, i64, i64, p, ctypes.c_size_t, p]
         L.h3f_residual_l1_noalloc.argtypes = [p, p, i64, p, i64, st, i64, i64, p]
         for name in EXPORTS[2:]:
@@ -573,6 +575,18 @@ def h3f_stream_read(src, sink, cached: bool = False, stream=None):
         _ptr(src), src.numel() * src.element_size(), 1 if cached else 0, _ptr(sink),
         _stream(dev, stream)))
     return src
+
+
+def h3f_stream_fill_bursts(dst, kib_per_wavefront: int, value: int = 0, stream=None):
+    """h3f_stream_fill with each wavefront writing its own kib_per_wavefront KiB
+    (1, 2, 5 or 10) before it ends (measurement helper)."""
+    dev = _dev(dst)
+    if not dst.is_contiguous():
+        raise ValueError("dst must be contiguous")
+    _check("h3f_stream_fill_bursts", lib().h3f_stream_fill_bursts(
+        _ptr(dst), dst.numel() * dst.element_size(), int(value) & 0xFFFFFFFF,
+        int(kib_per_wavefront), _stream(dev, stream)))
+    return dst
 
 
 def h3f_stream_fill(dst, value: int = 0, stream=None):

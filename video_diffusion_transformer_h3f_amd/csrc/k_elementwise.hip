@@ -199,6 +199,24 @@ stream_fill_kernel(char* __restrict__ dst, uint64_t bytes, unsigned value) {
     buf_st<kStoreStream>(rd, 16u * threadIdx.x, u32x4{value, value, value, value});
 }
 
+// Write-only stream in store bursts: wavefront w of workgroup b writes the K KiB
+// at (4 b + w) K KiB, K 16-byte stores per lane (each store 1 KiB contiguous
+// across the wavefront).  With K = 1 it is the fill above; larger K shows what
+// a wavefront that stores K KiB before it ends can write (the row-holding
+// kernels store 8-20 KiB per wavefront).
+template <int K>
+__global__ void __launch_bounds__(kDirBlock)
+stream_fill_burst_kernel(char* __restrict__ dst, uint64_t bytes, unsigned value) {
+    constexpr uint32_t kWaveBytes = K * 1024u;
+    const uint64_t t0 = ((uint64_t)blockIdx.x * (kDirBlock / 64) + (threadIdx.x >> 6)) * kWaveBytes;
+    const uint64_t left = t0 < bytes ? bytes - t0 : 0;
+    const rsrc_t rd = make_rsrc(dst + t0, left < kWaveBytes ? (uint32_t)left : kWaveBytes);
+    const uint32_t lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        buf_st<kStoreStream>(rd, 16u * (i * 64 + lane), u32x4{value, value, value, value});
+}
+
 inline unsigned blocks_for(int64_t chunks) {
     return (unsigned)((chunks + kTile - 1) / kTile);
 }
@@ -389,6 +407,29 @@ extern "C" h3f_status_t h3f_stream_read(const void* src, int64_t bytes, int32_t 
         hipLaunchKernelGGL(stream_read_kernel<kLoadStream>, dim3((unsigned)blocks), dim3(kDirBlock), 0, st,
                            static_cast<const char*>(src), (uint64_t)bytes, magic,
                            static_cast<unsigned*>(sink));
+    return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
+}
+
+extern "C" h3f_status_t h3f_stream_fill_bursts(void* dst, int64_t bytes, uint32_t value,
+                                              int32_t kib_per_wavefront, void* stream) {
+    if (bytes == 0) return H3F_OK;
+    if (!dst) return H3F_ERR_NULL_POINTER;
+    if (bytes < 0 || bytes % 16) return H3F_ERR_BAD_SHAPE;
+    if (!aligned16(dst)) return H3F_ERR_MISALIGNED;
+    const int k = kib_per_wavefront;
+    if (k != 1 && k != 2 && k != 5 && k != 10) return H3F_ERR_UNSUPPORTED;
+    const uint64_t wg_bytes = (uint64_t)(kDirBlock / 64) * k * 1024;
+    const uint64_t blocks = ((uint64_t)bytes + wg_bytes - 1) / wg_bytes;
+    if (blocks > 0xffffffffull) return H3F_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* d = static_cast<char*>(dst);
+    const dim3 g((unsigned)blocks), b(kDirBlock);
+    switch (k) {
+        case 1: hipLaunchKernelGGL(stream_fill_burst_kernel<1>, g, b, 0, st, d, (uint64_t)bytes, value); break;
+        case 2: hipLaunchKernelGGL(stream_fill_burst_kernel<2>, g, b, 0, st, d, (uint64_t)bytes, value); break;
+        case 5: hipLaunchKernelGGL(stream_fill_burst_kernel<5>, g, b, 0, st, d, (uint64_t)bytes, value); break;
+        default: hipLaunchKernelGGL(stream_fill_burst_kernel<10>, g, b, 0, st, d, (uint64_t)bytes, value); break;
+    }
     return hipGetLastError() == hipSuccess ? H3F_OK : H3F_ERR_LAUNCH;
 }
 
