@@ -13,8 +13,12 @@
 // in LDS and its wavefronts read them from there; otherwise every row reads
 // its group's vectors through the cache hierarchy (L1/L2, not HBM).
 // Measured on MI355X: one row per wavefront, no grid-stride reuse, is the
-// fastest organisation (multi-wavefront rows pay more in barriers than they
-// gain in finer-grained streaming).  The order in which a wavefront issues its
+// fastest organisation (multi-wavefront rows pay more in barriers or in
+// modulation staging than they gain in finer-grained streaming).  What sets
+// its time is the 10 KiB (hidden 5120, bf16) each wavefront stores: a
+// wavefront that stores 10 KiB writes at about 5.5 TB/s against 7.1 TB/s at
+// 1 KiB, and reading the row bytes at the read-only rate then writing them at
+// that rate gives the time the kernel takes.  The order in which a wavefront issues its
 // row loads matters by ~3%: they go out strictly in address order (scheduling
 // barriers keep the compiler from interleaving them).  The plain kernel stages
 // the modulation first and then issues a bf16 row at raised wave priority, so

@@ -242,9 +242,13 @@ __global__ void __launch_bounds__(64) qk_rmsnorm_rope3d_kernel(QKArgs a) {
 // workspace layout.  Many wavefronts per block are needed: a token's work is a
 // chain of dependent steps (sincos, lane shuffles, the RMS reduction), and one
 // wavefront walking a whole block alone left the chip mostly waiting on them.
-// Measured at the 5 s shape (tokens per chunk x wavefronts): 8 x 1 1.03 ms,
-// 8 x 4 0.99, 4 x 8 0.95, 2 x 8 0.92, 1 x 16 0.93, 2 x 16 0.91 (the plain
-// operator alone: 0.80 ms, plus 0.41 ms for the router's separate pooling).
+// Measured side by side at the 5 s shape (tokens per chunk x wavefronts),
+// before the per-token code was tuned further: 8 x 1 1.03 ms, 8 x 4 0.99,
+// 4 x 8 0.95, 2 x 8 0.92, 1 x 16 0.93, 2 x 16 0.91.  The tuned 2 x 16 form runs
+// 0.86-0.87 ms, against 0.76 ms for the plain operator plus 0.41 ms for the
+// router's separate pooling.  Each wavefront stores 8 KiB (its 8 tokens),
+// and wavefronts that store several KiB write more slowly than ones that
+// store one (about 5.5 against 7.1 TB/s at 10 KiB and 1 KiB per wavefront).
 constexpr int kPoolTokens = 2;
 constexpr int kPoolWaves = 16;
 
